@@ -1,0 +1,183 @@
+"""Exact causal softmax attention in float64.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
+
+What is computed (the causal forward/prefill attention pass of the pages:
+Le Fil IA summary paragraph; aicronaca.it "Che cosa ha annunciato Zyphra";
+ai4bro.com "TL;DR"). The pages describe the tiled method -- Q.K^T, a row
+softmax, P.V -- whose exact result is plain softmax attention, so the oracle is
+that definition written out, with no tiling and no online rescaling:
+
+    for batch b, query head h, kv head g = floor(h / G), G = Hq / Hkv:
+      s[i, j]  = softmax_scale * dot(Q[b, i, h, :], K[b, j, g, :])   for j <= i
+      m[i]     = max_j s[i, j]
+      l[i]     = sum_j exp(s[i, j] - m[i])
+      O[b,i,h] = sum_j exp(s[i, j] - m[i]) * V[b, j, g, :] / l[i]
+      LSE[b,h,i] = m[i] + ln l[i]
+
+Readings where the pages are silent (each listed in the design notes):
+
+* tensor layout is that of ``flash_attn_func`` (the pages call the library a
+  drop-in for it): q [B,S,Hq,d_qk], k [B,S,Hkv,d_qk], v [B,S,Hkv,d_v];
+* grouped-query heads map contiguously, kv head = floor(h / G);
+* the softmax scale is 1/sqrt(d_qk) (1/sqrt(192) for the MLA shape);
+* causal alignment is square (S_q = S_k): key j is visible to query i iff
+  j <= i, so no row is empty;
+* LSE is the natural logarithm and includes every scale.
+
+Subtracting the row maximum is an exact identity (it cancels between the
+numerator and l); it only keeps exp() in range.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .formats import bf16_decode, bf16_encode, dequantize_fp8, quantize_fp8_per_tensor
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B, S, H, d]")
+    B, S, Hq, dqk = q.shape
+    if k.shape[:2] != (B, S) or v.shape[:2] != (B, S):
+        raise ValueError("q, k, v must share B and S")
+    Hkv = k.shape[2]
+    if v.shape[2] != Hkv or k.shape[3] != dqk:
+        raise ValueError("k/v head count or k head dim mismatch")
+    if Hkv == 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return B, S, Hq, Hkv, dqk, v.shape[3]
+
+
+def _rows_softmax_attention(qrows, K, V, ends, scale):
+    """Exact attention for a set of query rows against keys [0, end_r).
+
+    qrows [R, d_qk]; K [S, d_qk]; V [S, d_v]; ends[r] = number of visible keys.
+    Returns (O [R, d_v], LSE [R]) in float64.
+    """
+    R = qrows.shape[0]
+    n = int(max(ends)) if R else 0
+    s = (qrows @ K[:n].T) * scale  # [R, n]
+    visible = np.arange(n)[None, :] < np.asarray(ends)[:, None]
+    s = np.where(visible, s, -np.inf)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])  # exp(-inf) = 0 for hidden keys
+    l = p.sum(axis=1)
+    o = (p @ V[:n]) / l[:, None]
+    return o, m + np.log(l)
+
+
+def causal_attention(q, k, v, causal: bool = True, softmax_scale: float | None = None,
+                     row_block: int = 512):
+    """Softmax attention of float64 tensors in the flash_attn_func layout.
+
+    Returns (O [B,S,Hq,d_v] float64, LSE [B,Hq,S] float64). Rows are processed
+    ``row_block`` at a time only to bound memory; each row is computed by the
+    definition above.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S, Hq, Hkv, dqk, dv = _check_shapes(q, k, v)
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
+    O = np.zeros((B, S, Hq, dv), dtype=np.float64)
+    L = np.zeros((B, Hq, S), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            K = np.ascontiguousarray(k[b, :, g, :])
+            V = np.ascontiguousarray(v[b, :, g, :])
+            for i0 in range(0, S, row_block):
+                i1 = min(S, i0 + row_block)
+                rows = np.arange(i0, i1)
+                ends = rows + 1 if causal else np.full(i1 - i0, S)
+                o, lse = _rows_softmax_attention(q[b, i0:i1, h, :], K, V, ends, scale)
+                O[b, i0:i1, h, :] = o
+                L[b, h, i0:i1] = lse
+    return O, L
+
+
+def attention_rows(q, k, v, rows, causal: bool = True, softmax_scale: float | None = None):
+    """Exact attention for selected (b, h, i) rows only.
+
+    ``q``, ``k``, ``v`` may be any array-likes indexable as [b, :, h, :]
+    (for example the dequantizing views made by ``prefill_reference``);
+    only the heads the rows touch are materialised in float64.
+    Returns (O [R, d_v], LSE [R]).
+    """
+    Hq = q.shape[2]
+    Hkv = k.shape[2]
+    S = q.shape[1]
+    G = Hq // Hkv
+    dqk = q.shape[3]
+    scale = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
+    rows = [tuple(int(t) for t in r) for r in rows]
+    outs = [None] * len(rows)
+    lses = np.zeros(len(rows))
+    by_head: dict[tuple[int, int], list[int]] = {}
+    for idx, (b, h, i) in enumerate(rows):
+        by_head.setdefault((b, h), []).append(idx)
+    for (b, h), idxs in by_head.items():
+        g = h // G
+        K = np.asarray(k[b, :, g, :], dtype=np.float64)
+        V = np.asarray(v[b, :, g, :], dtype=np.float64)
+        Q = np.asarray(q[b, :, h, :], dtype=np.float64)
+        ii = np.array([rows[t][2] for t in idxs])
+        ends = ii + 1 if causal else np.full(len(ii), S)
+        o, lse = _rows_softmax_attention(Q[ii], K, V, ends, scale)
+        for t, idx in enumerate(idxs):
+            outs[idx] = o[t]
+            lses[idx] = lse[t]
+    return np.stack(outs), lses
+
+
+class _Dequantized:
+    """Array-like view that dequantizes e4m3fn codes or bf16 bits on indexing."""
+
+    def __init__(self, codes, scale=None, kind="fp8"):
+        self.codes = codes
+        self.scale = scale
+        self.kind = kind
+        self.shape = codes.shape
+
+    def __getitem__(self, idx):
+        c = self.codes[idx]
+        if self.kind == "fp8":
+            return dequantize_fp8(c, self.scale)
+        return bf16_decode(c)
+
+
+def prefill_reference(q32, k32, v32, dtype: str, causal: bool = True, rows=None,
+                      softmax_scale: float | None = None):
+    """The whole path on float32 inputs: quantize each tensor, then attend.
+
+    dtype "fp8": per-tensor absmax e4m3fn codes and scales; "bf16": bf16 RNE.
+    Attention runs in float64 on the dequantized values. With ``rows`` given,
+    only those (b, h, i) rows are computed. Returns a dict with the codes
+    (uint8 for fp8, uint16 bit patterns for bf16), the scales (1.0 for bf16),
+    and either the full O/LSE or the selected rows.
+    """
+    out = {}
+    if dtype == "fp8":
+        (qc, qs), (kc, ks), (vc, vs) = (quantize_fp8_per_tensor(t) for t in (q32, k32, v32))
+        views = [_Dequantized(qc, qs), _Dequantized(kc, ks), _Dequantized(vc, vs)]
+    elif dtype == "bf16":
+        qc, kc, vc = (bf16_encode(t) for t in (q32, k32, v32))
+        qs = ks = vs = np.float32(1.0)
+        views = [_Dequantized(qc, kind="bf16"), _Dequantized(kc, kind="bf16"),
+                 _Dequantized(vc, kind="bf16")]
+    else:
+        raise ValueError("dtype must be 'fp8' or 'bf16'")
+    out.update(q_codes=qc, k_codes=kc, v_codes=vc, q_scale=qs, k_scale=ks, v_scale=vs)
+    if rows is None:
+        qd, kd, vd = (vw[:] for vw in views)
+        O, L = causal_attention(qd, kd, vd, causal=causal, softmax_scale=softmax_scale)
+        out.update(o=O, lse=L)
+    else:
+        O, L = attention_rows(*views, rows=rows, causal=causal, softmax_scale=softmax_scale)
+        out.update(o_rows=O, lse_rows=L)
+    return out
