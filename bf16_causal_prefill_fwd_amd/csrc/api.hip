@@ -1,0 +1,168 @@
+// C ABI of libattn_prefill.so (declared in include/attn_prefill.h): argument
+// checks, device check, kernel variant selection, work partition and launch.
+#include <math.h>
+#include <mutex>
+#include <string.h>
+
+#include "attn_prefill.h"
+#include "attn_fwd_kernel.h"
+#include "quantize.h"
+
+namespace attn {
+
+// Kernel variants: (dtype, d_qk, d_v) -> tile configuration.
+using CfgF8D128 = FwdCfg<true, 128, 128, 128, 128>;
+using CfgF8D192 = FwdCfg<true, 192, 128, 128, 64>;
+using CfgBFD128 = FwdCfg<false, 128, 128, 128, 64>;
+using CfgBFD192 = FwdCfg<false, 192, 128, 128, 64>;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+int g_dev_state[kMaxDevices];  // 0 unknown, 1 ready (gfx950), -1 unsupported
+
+template <class C>
+hipError_t prepare_kernel() {
+  return hipFuncSetAttribute((const void*)attn_fwd_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             C::LDS_BYTES);
+}
+
+// Once per device: confirm gfx950 and raise the dynamic LDS limit of every
+// attention variant to its tile size.
+int device_ready() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_dev_state[dev] == 1) return ATTN_OK;
+  if (g_dev_state[dev] == -1) return ATTN_ERR_UNSUPPORTED;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    g_dev_state[dev] = -1;
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (prepare_kernel<CfgF8D128>() != hipSuccess || prepare_kernel<CfgF8D192>() != hipSuccess ||
+      prepare_kernel<CfgBFD128>() != hipSuccess || prepare_kernel<CfgBFD192>() != hipSuccess)
+    return ATTN_ERR_HIP;
+  g_dev_state[dev] = 1;
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool good_scale(float s) { return isfinite(s) && s > 0.f; }
+
+template <class C>
+int launch_fwd(FwdParams prm, hipStream_t stream) {
+  prm.n_mtiles = (prm.S + C::BM - 1) / C::BM;
+  const int64_t units = (int64_t)prm.B * prm.Hkv;
+  const int64_t items = (int64_t)prm.B * prm.Hq * prm.n_mtiles;
+  if (items > 0x7FFFFFFF) return ATTN_ERR_INVALID;
+  prm.xcd_remap = (units % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL(attn_fwd_kernel<C>, dim3((unsigned)items), dim3(C::NTHREADS), C::LDS_BYTES, stream, prm);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale, float k_scale,
+             float v_scale, const float* d_scales, float softmax_scale, int B, int S, int Hq, int Hkv, int d_qk,
+             int d_v, int causal, int dtype, hipStream_t stream) {
+  // ---- host-side checks, before any HIP call
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || d_qk <= 0 || d_v <= 0) return ATTN_ERR_INVALID;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
+  if (S > (1 << 24)) return ATTN_ERR_INVALID;
+  if (!d_scales && !(good_scale(q_scale) && good_scale(k_scale) && good_scale(v_scale))) return ATTN_ERR_INVALID;
+  if (!good_scale(softmax_scale)) return ATTN_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+    return ATTN_ERR_INVALID;
+  const double elems = (double)B * S * Hq * (d_qk > d_v ? d_qk : d_v);
+  if (elems >= 1099511627776.0) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_DTYPE_FP8_E4M3 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!((d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128))) return ATTN_ERR_UNSUPPORTED;
+
+  const int ready = device_ready();
+  if (ready != ATTN_OK) return ready;
+
+  FwdParams prm{};
+  prm.q = (const uint8_t*)q;
+  prm.k = (const uint8_t*)k;
+  prm.v = (const uint8_t*)v;
+  prm.o = (uint16_t*)o;
+  prm.lse = lse;
+  prm.d_scales = d_scales;
+  prm.q_scale = q_scale;
+  prm.k_scale = k_scale;
+  prm.v_scale = v_scale;
+  prm.sm_scale = softmax_scale;
+  prm.B = B;
+  prm.S = S;
+  prm.Hq = Hq;
+  prm.Hkv = Hkv;
+  prm.causal = causal;
+
+  if (dtype == ATTN_DTYPE_FP8_E4M3)
+    return d_qk == 128 ? launch_fwd<CfgF8D128>(prm, stream) : launch_fwd<CfgF8D192>(prm, stream);
+  return d_qk == 128 ? launch_fwd<CfgBFD128>(prm, stream) : launch_fwd<CfgBFD192>(prm, stream);
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" {
+
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale,
+                     float k_scale, float v_scale, int B, int S, int Hq, int Hkv, int d_qk, int d_v, int causal,
+                     int dtype, hipStream_t stream) {
+  const float sm = d_qk > 0 ? (float)(1.0 / sqrt((double)d_qk)) : 0.f;
+  return attn::fwd_impl(q, k, v, o, lse, q_scale, k_scale, v_scale, nullptr, sm, B, S, Hq, Hkv, d_qk, d_v,
+                        causal, dtype, stream);
+}
+
+int attn_prefill_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale,
+                        float k_scale, float v_scale, const float* d_scales, float softmax_scale, int B, int S,
+                        int Hq, int Hkv, int d_qk, int d_v, int causal, int dtype, hipStream_t stream) {
+  if (d_scales && ((uintptr_t)d_scales & 3u)) return ATTN_ERR_INVALID;
+  return attn::fwd_impl(q, k, v, o, lse, q_scale, k_scale, v_scale, d_scales, softmax_scale, B, S, Hq, Hkv, d_qk,
+                        d_v, causal, dtype, stream);
+}
+
+int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, hipStream_t stream) {
+  if (!x || !x8 || !d_scale) return ATTN_ERR_INVALID;
+  if (n <= 0 || n >= ((int64_t)1 << 40)) return ATTN_ERR_INVALID;
+  if (x_dtype != 0 && x_dtype != 1) return ATTN_ERR_UNSUPPORTED;
+  if (((uintptr_t)x & 15u) || ((uintptr_t)x8 & 15u) || ((uintptr_t)d_scale & 3u)) return ATTN_ERR_INVALID;
+  const char* xb = (const char*)x;
+  const char* xe = xb + n * (x_dtype == 0 ? 4 : 2);
+  const char* sb = (const char*)d_scale;
+  const char* ob = (const char*)x8;
+  if ((sb + 4 > xb && sb < xe) || (sb + 4 > ob && sb < ob + n)) return ATTN_ERR_INVALID;
+  const int ready = attn::device_ready();
+  if (ready != ATTN_OK) return ready;
+  return attn::launch_quantize_fp8(x, x_dtype, n, x8, d_scale, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream) {
+  if (!x || !y) return ATTN_ERR_INVALID;
+  if (n <= 0 || n >= ((int64_t)1 << 40)) return ATTN_ERR_INVALID;
+  if (((uintptr_t)x & 15u) || ((uintptr_t)y & 15u)) return ATTN_ERR_INVALID;
+  const int ready = attn::device_ready();
+  if (ready != ATTN_OK) return ready;
+  return attn::launch_cast_bf16(x, n, y, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, head dims or device (needs gfx950)";
+    case ATTN_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown error code";
+  }
+}
+
+int attn_abi_version(void) { return 1; }
+
+}  // extern "C"

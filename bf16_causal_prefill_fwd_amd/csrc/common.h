@@ -1,0 +1,73 @@
+// Shared device-side types and small helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+// 32x32x64 FP8 (e4m3 x e4m3) MFMA, fp32 accumulate. Operand lane layout on
+// gfx950 (established on hardware): A lane l holds row l%32, B lane l holds
+// column l%32; the 32 bytes of lanes 0..31 and of lanes 32..63 are two
+// disjoint halves of the 64-deep contraction, paired byte for byte between A
+// and B. C/D lane l holds column l%32, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4. Scale operands 0 select the unscaled form.
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 32x32x16 BF16 MFMA, fp32 accumulate; same row/column/accumulator layout,
+// 8 contraction elements per lane per half.
+__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b8: within each 16-lane group, lane k supplies the address
+// of 8 bytes forming half k%2 of row k/2 of an 8 x 16 byte tile; lane i
+// receives column i (byte j from row j).
+__device__ __forceinline__ i32x2 lds_read_tr8(const ATTN_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((ATTN_LDS i32x2*)p);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane k supplies the address
+// of 4 16-bit elements forming quarter k%4 of row k/4 of a 4 x 16 element
+// tile; lane i receives column i (element j from row j).
+__device__ __forceinline__ i16x4 lds_read_tr16(const ATTN_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)p);
+}
+
+__device__ __forceinline__ i32x4 lds_read_b128(const ATTN_LDS char* p) {
+  return *(const ATTN_LDS i32x4*)p;
+}
+
+__device__ __forceinline__ void lds_write_b128(ATTN_LDS char* p, const i32x4& v) {
+  *(ATTN_LDS i32x4*)p = v;
+}
+
+// Value of the other half-wave's lane (l ^ 32).
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  // lane < 32: r[1] holds lane l+32; lane >= 32: r[0] holds lane l-32
+  return __int_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+// Two fp32 values -> two e4m3fn bytes (round to nearest even), placed in
+// bytes 0,1 (hi = false) or 2,3 (hi = true) of `old`.
+__device__ __forceinline__ int cvt_fp8x2(float a, float b, int old, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, true)
+            : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace attn

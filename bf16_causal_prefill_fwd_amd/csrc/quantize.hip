@@ -1,0 +1,168 @@
+// Input step of the attention path: per-tensor FP8 e4m3fn quantization and
+// the fp32 -> bf16 cast.
+//
+// The pages fix the FP8 format (e4m3: ai4bro.com "TL;DR"; Le Fil IA, context
+// paragraph) but not the scale granularity; this library uses one fp32 scale
+// per tensor: scale = absmax / 448 (448 = largest e4m3fn value), code =
+// e4m3fn(x / scale) rounded to nearest even.
+//
+// Two HBM passes: a grid-wide absmax (each workgroup folds its maximum in
+// with one integer atomic max on the IEEE bits, which orders non-negative
+// floats like their values, so the result is independent of timing), then the
+// cast. Both passes stream 16-byte vectors and are bound by HBM bandwidth.
+#include "common.h"
+#include "quantize.h"
+
+namespace attn {
+
+constexpr int QTHREADS = 256;
+
+__global__ void amax_reset_kernel(uint32_t* amax_bits) { *amax_bits = 0u; }
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t u16) { return __uint_as_float(u16 << 16); }
+
+// x: 8 elements per thread-iteration (fp32: two 16-byte loads; bf16: one).
+template <int XDT>
+__global__ __launch_bounds__(QTHREADS) void amax_kernel(const void* __restrict__ x, int64_t n,
+                                                         uint32_t* amax_bits) {
+  float m = 0.f;
+  const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
+  const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
+  const int64_t n8 = n / 8;
+  for (int64_t i = gtid; i < n8; i += nthreads) {
+    if constexpr (XDT == 0) {
+      const float4* p = (const float4*)x + 2 * i;
+      float4 a = p[0], c = p[1];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+    } else {
+      uint4 a = ((const uint4*)x)[i];
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = fmaxf(m, fabsf(bf16_bits_to_float(w[j] & 0xFFFFu)));
+        m = fmaxf(m, fabsf(bf16_bits_to_float(w[j] >> 16)));
+      }
+    }
+  }
+  for (int64_t i = n8 * 8 + gtid; i < n; i += nthreads) {
+    float v = XDT == 0 ? ((const float*)x)[i] : bf16_bits_to_float(((const uint16_t*)x)[i]);
+    m = fmaxf(m, fabsf(v));
+  }
+  // wave reduction, then across the workgroup's 4 waves
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float red[QTHREADS / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < QTHREADS / 64; ++w) r = fmaxf(r, red[w]);
+    atomicMax(amax_bits, __float_as_uint(r));
+  }
+}
+
+__device__ __forceinline__ float scale_from_amax(uint32_t bits) {
+  const float a = __uint_as_float(bits);
+  return a == 0.f ? 1.f : __fdiv_rn(a, 448.f);
+}
+
+template <int XDT>
+__global__ __launch_bounds__(QTHREADS) void quant_kernel(const void* __restrict__ x, int64_t n,
+                                                          const uint32_t* __restrict__ amax_bits,
+                                                          uint8_t* __restrict__ out) {
+  const float scale = scale_from_amax(*amax_bits);
+  const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
+  const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
+  const int64_t n8 = n / 8;
+  for (int64_t i = gtid; i < n8; i += nthreads) {
+    float v[8];
+    if constexpr (XDT == 0) {
+      const float4* p = (const float4*)x + 2 * i;
+      float4 a = p[0], c = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    } else {
+      uint4 a = ((const uint4*)x)[i];
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
+        v[2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __fdiv_rn(v[j], scale);
+    int lo = cvt_fp8x2(v[0], v[1], 0, false);
+    lo = cvt_fp8x2(v[2], v[3], lo, true);
+    int hi = cvt_fp8x2(v[4], v[5], 0, false);
+    hi = cvt_fp8x2(v[6], v[7], hi, true);
+    ((uint2*)out)[i] = make_uint2((uint32_t)lo, (uint32_t)hi);
+  }
+  for (int64_t i = n8 * 8 + gtid; i < n; i += nthreads) {
+    float v = XDT == 0 ? ((const float*)x)[i] : bf16_bits_to_float(((const uint16_t*)x)[i]);
+    out[i] = (uint8_t)(cvt_fp8x2(__fdiv_rn(v, scale), 0.f, 0, false) & 0xFF);
+  }
+}
+
+__global__ void scale_finalize_kernel(uint32_t* amax_bits) {
+  *amax_bits = __float_as_uint(scale_from_amax(*amax_bits));
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__global__ __launch_bounds__(QTHREADS) void cast_bf16_kernel(const float* __restrict__ x, int64_t n,
+                                                              uint16_t* __restrict__ y) {
+  const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
+  const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
+  const int64_t n8 = n / 8;
+  for (int64_t i = gtid; i < n8; i += nthreads) {
+    const float4* p = (const float4*)x + 2 * i;
+    float4 a = p[0], c = p[1];
+    uint4 o;
+    o.x = f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16);
+    o.y = f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16);
+    o.z = f32_to_bf16_rne(c.x) | (f32_to_bf16_rne(c.y) << 16);
+    o.w = f32_to_bf16_rne(c.z) | (f32_to_bf16_rne(c.w) << 16);
+    ((uint4*)y)[i] = o;
+  }
+  for (int64_t i = n8 * 8 + gtid; i < n; i += nthreads) y[i] = (uint16_t)f32_to_bf16_rne(x[i]);
+}
+
+static int stream_grid(int64_t n) {
+  // enough workgroups to cover all 256 CUs several times over, capped by the work
+  const int64_t per_block = (int64_t)QTHREADS * 8 * 4;
+  int64_t g = (n + per_block - 1) / per_block;
+  if (g > 256 * 16) g = 256 * 16;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
+                               hipStream_t stream) {
+  uint32_t* bits = (uint32_t*)d_scale;
+  const int grid = stream_grid(n);
+  hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, bits);
+  if (x_dtype == 0) {
+    hipLaunchKernelGGL(amax_kernel<0>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits);
+    hipLaunchKernelGGL(quant_kernel<0>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits, x8);
+  } else {
+    hipLaunchKernelGGL(amax_kernel<1>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits);
+    hipLaunchKernelGGL(quant_kernel<1>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits, x8);
+  }
+  hipLaunchKernelGGL(scale_finalize_kernel, dim3(1), dim3(1), 0, stream, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream) {
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3(stream_grid(n)), dim3(QTHREADS), 0, stream, x, n, y);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,125 @@
+/*
+ * attn_prefill.h -- C ABI of libattn_prefill.so: causal prefill attention
+ * forward for AMD Instinct MI355X (gfx950), FP8 e4m3 and BF16.
+ *
+ * What is computed: the causal forward (prefill) attention pass the ZYFA
+ * pages describe -- tiled Q.K^T, a row softmax with running max and row sum,
+ * then P.V -- in FP8 e4m3 and BF16, for head dim 128 with grouped-query heads
+ * and for the MLA shape (Q.K dim 192, V dim 128). Sources: Le Fil IA (ZYFA:
+ * FlashAttention en FP8 pour l'AMD MI355X), summary paragraph; aicronaca.it,
+ * section "Che cosa ha annunciato Zyphra"; ai4bro.com, section "TL;DR".
+ *
+ *   s[i,j]   = softmax_scale * q_scale * k_scale * dot(q[b,i,h,:], k[b,j,g,:]),
+ *              g = h / (Hq/Hkv), visible iff j <= i (causal) or always;
+ *   o[b,i,h] = v_scale * sum_j softmax_j(s[i,:]) * v[b,j,g,:]       (bf16)
+ *   lse[b,h,i] = ln sum_j exp(s[i,j])                                (fp32)
+ *
+ * with softmax_scale = 1/sqrt(d_qk) in attn_prefill_fwd.
+ *
+ * Conventions shared by every entry point:
+ *  - Layouts are those of flash_attn_func (the pages present the library as
+ *    a drop-in for it), contiguous, row-major:
+ *      q [B, S, Hq,  d_qk]   k [B, S, Hkv, d_qk]   v [B, S, Hkv, d_v]
+ *      o [B, S, Hq,  d_v]  bfloat16          lse [B, Hq, S]  float32
+ *  - FP8 is OCP e4m3fn (1 byte, bias 7, max 448, no infinities). A value is
+ *    code * scale with one float scale per tensor.
+ *  - Every pointer argument except `stream` is DEVICE memory owned by the
+ *    caller. The library allocates nothing, keeps no pointer after return,
+ *    and does not synchronise: work is enqueued on `stream` (0 = the null
+ *    stream) and the call returns.
+ *  - Return value: 0 on success, or a negative ATTN_ERR_* code. Argument
+ *    checks run on the host before anything is enqueued; a failed check
+ *    enqueues nothing. ATTN_ERR_HIP reports a launch failure
+ *    (hipGetLastError after the launch).
+ *  - Runs are deterministic: no atomics touch values, each output element
+ *    has one fixed reduction order, so repeated launches are bit-identical.
+ */
+#ifndef ATTN_PREFILL_H
+#define ATTN_PREFILL_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = -1,      /* null pointer, non-positive size, Hq % Hkv != 0, causal not 0/1 */
+  ATTN_ERR_UNSUPPORTED = -2,  /* dtype or (d_qk, d_v) not built, device is not gfx950 */
+  ATTN_ERR_HIP = -3,          /* a HIP call or kernel launch failed */
+};
+
+enum {
+  ATTN_DTYPE_FP8_E4M3 = 0,    /* q, k, v are uint8 e4m3fn codes */
+  ATTN_DTYPE_BF16 = 1,        /* q, k, v are bfloat16 */
+};
+
+/*
+ * Causal (or full) prefill attention forward.
+ *   q, k, v     device inputs in the layouts above, element type per `dtype`.
+ *   o           device output, bfloat16 [B, S, Hq, d_v].
+ *   lse         device output float32 [B, Hq, S], natural log, including the
+ *               softmax and dequantization scales; NULL skips it.
+ *   q_scale, k_scale, v_scale
+ *               per-tensor dequantization scales (value = code * scale);
+ *               pass 1.0 for BF16. Must be finite and > 0.
+ *   B, S, Hq, Hkv  batch, sequence length (queries = keys), query heads,
+ *               key/value heads; Hq must be a multiple of Hkv (grouped-query
+ *               attention, query head h reads kv head h / (Hq/Hkv)).
+ *   d_qk, d_v   head dims; supported: (128, 128) and (192, 128).
+ *   causal      1: key j visible to query i iff j <= i; 0: all keys visible.
+ *   dtype       ATTN_DTYPE_FP8_E4M3 or ATTN_DTYPE_BF16.
+ * Limits: B*S*Hq*max(d_qk,d_v) < 2^40 elements; S <= 2^24.
+ */
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     float q_scale, float k_scale, float v_scale,
+                     int B, int S, int Hq, int Hkv, int d_qk, int d_v,
+                     int causal, int dtype, hipStream_t stream);
+
+/*
+ * As attn_prefill_fwd, with an explicit softmax scale (> 0, finite) and the
+ * three dequantization scales read from DEVICE memory (each a pointer to one
+ * float, e.g. the output of attn_quantize_fp8), so a quantize -> attention
+ * sequence needs no host synchronisation. Passing d_scales == NULL uses
+ * q_scale, k_scale, v_scale from the host arguments instead.
+ *   d_scales    NULL, or device float[3] = {q_scale, k_scale, v_scale}.
+ */
+int attn_prefill_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                        float q_scale, float k_scale, float v_scale, const float* d_scales,
+                        float softmax_scale,
+                        int B, int S, int Hq, int Hkv, int d_qk, int d_v,
+                        int causal, int dtype, hipStream_t stream);
+
+/*
+ * Per-tensor FP8 quantize-and-layout step (the input side of the FP8 path).
+ *   x        device input, n elements, float32 (x_dtype 0) or bfloat16 (1).
+ *   n        element count, 0 < n < 2^40.
+ *   x8       device output, n uint8 e4m3fn codes, same layout as x.
+ *   d_scale  device output, one float: absmax(|x|)/448 in fp32 (1.0 when x
+ *            is all zeros). Also used as the absmax accumulator while the
+ *            call's kernels run, so it must not alias x or x8.
+ * code = e4m3fn(x / scale), division in fp32 correctly rounded, rounding to
+ * nearest with ties to even. Inputs must be finite. Deterministic.
+ */
+int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
+                      hipStream_t stream);
+
+/*
+ * BF16 input step: float32 -> bfloat16, round to nearest, ties to even.
+ *   x  device float32[n];  y  device bfloat16[n] (as uint16 bits);  0 < n < 2^40.
+ */
+int attn_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream);
+
+/* Human-readable text of a return code (static storage). */
+const char* attn_strerror(int code);
+
+/* ABI version of this header: 1. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_PREFILL_H */

@@ -1,0 +1,85 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/attn_prefill.h
+declares, and reject bad arguments with ATTN_ERR_INVALID / _UNSUPPORTED
+before any HIP call is made (all calls here use arguments that fail the
+host checks, so nothing reaches a device).
+"""
+
+import ctypes
+import os
+
+import pytest
+
+from bf16_causal_prefill_fwd_amd import build as build_mod
+from bf16_causal_prefill_fwd_amd import ops
+
+pytestmark = pytest.mark.skipif(not os.path.exists(build_mod.LIB_PATH), reason="library not built")
+
+INVALID, UNSUPPORTED = -1, -2
+FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced by host checks
+
+
+def test_exports_every_header_function():
+    names = ops.header_functions()
+    assert set(names) == {"attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_quantize_fp8", "attn_cast_bf16",
+                          "attn_strerror", "attn_abi_version"}
+    L = ctypes.CDLL(build_mod.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) <= set(ops._SIGNATURES)
+
+
+def test_version_and_strerror():
+    L = ops.lib()
+    assert L.attn_abi_version() == 1
+    assert ops.strerror(0) == "success"
+    assert "invalid" in ops.strerror(INVALID)
+    assert "gfx950" in ops.strerror(UNSUPPORTED)
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, qs=1.0, ks=1.0, vs=1.0, B=1, S=64, Hq=4, Hkv=2,
+             dqk=128, dv=128, causal=1, dtype=0)
+    a.update(kw)
+    return ops.lib().attn_prefill_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["qs"], a["ks"], a["vs"],
+                                      a["B"], a["S"], a["Hq"], a["Hkv"], a["dqk"], a["dv"], a["causal"],
+                                      a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(B=0), INVALID),
+    (dict(S=-1), INVALID),
+    (dict(Hq=6, Hkv=4), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(qs=0.0), INVALID),
+    (dict(vs=float("nan")), INVALID),
+    (dict(q=FAKE + 4), INVALID),
+    (dict(S=(1 << 24) + 1), INVALID),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(dqk=64, dv=64), UNSUPPORTED),
+    (dict(dqk=192, dv=192), UNSUPPORTED),
+])
+def test_fwd_rejects_bad_arguments(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_fwd_ex_rejects_bad_softmax_scale_and_scale_pointer():
+    L = ops.lib()
+    f = L.attn_prefill_fwd_ex
+    args = [FAKE, FAKE, FAKE, FAKE, None, 1.0, 1.0, 1.0, None]
+    assert f(*args, 0.0, 1, 64, 2, 2, 128, 128, 1, 0, None) == INVALID
+    assert f(*args[:8], FAKE + 2, 0.1, 1, 64, 2, 2, 128, 128, 1, 0, None) == INVALID
+
+
+def test_quantize_and_cast_reject_bad_arguments():
+    L = ops.lib()
+    assert L.attn_quantize_fp8(None, 0, 16, FAKE, FAKE, None) == INVALID
+    assert L.attn_quantize_fp8(FAKE, 0, 0, FAKE, FAKE, None) == INVALID
+    assert L.attn_quantize_fp8(FAKE, 2, 16, FAKE, FAKE + 1024, None) == UNSUPPORTED
+    assert L.attn_quantize_fp8(FAKE + 8, 0, 16, FAKE, FAKE + 1024, None) == INVALID
+    assert L.attn_quantize_fp8(FAKE, 0, 16, FAKE + 1024, FAKE + 8, None) == INVALID  # scale aliases x
+    assert L.attn_cast_bf16(None, 8, FAKE, None) == INVALID
+    assert L.attn_cast_bf16(FAKE, -5, FAKE, None) == INVALID
