@@ -39,6 +39,8 @@ from .formats import (
     bf16_decode,
     bf16_encode,
     quantize_fp8_per_tensor,
+    per_tensor_scale,
+    encode_with_scale,
     dequantize_fp8,
 )
 from .attention import (
@@ -54,6 +56,8 @@ __all__ = [
     "bf16_decode",
     "bf16_encode",
     "quantize_fp8_per_tensor",
+    "per_tensor_scale",
+    "encode_with_scale",
     "dequantize_fp8",
     "causal_attention",
     "attention_rows",

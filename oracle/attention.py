@@ -35,7 +35,7 @@ import math
 
 import numpy as np
 
-from .formats import bf16_decode, bf16_encode, dequantize_fp8, quantize_fp8_per_tensor
+from .formats import bf16_decode, bf16_encode, dequantize_fp8, encode_with_scale, per_tensor_scale
 
 
 def _check_shapes(q, k, v):
@@ -135,17 +135,28 @@ def attention_rows(q, k, v, rows, causal: bool = True, softmax_scale: float | No
     return np.stack(outs), lses
 
 
-class _Dequantized:
-    """Array-like view that dequantizes e4m3fn codes or bf16 bits on indexing."""
+class _QuantizedView:
+    """Array-like view of a float32 tensor after the input step.
 
-    def __init__(self, codes, scale=None, kind="fp8"):
-        self.codes = codes
-        self.scale = scale
+    Indexing returns the dequantized float64 values of the selected elements:
+    fp8 -> decode(e4m3fn(x / scale)) * scale with the per-tensor scale of the
+    WHOLE tensor; bf16 -> the bf16-rounded values. Only the requested slice is
+    encoded, so rows of very long sequences stay cheap.
+    """
+
+    def __init__(self, x32, kind):
+        self.x32 = np.asarray(x32, dtype=np.float32)
         self.kind = kind
-        self.shape = codes.shape
+        self.shape = self.x32.shape
+        self.scale = per_tensor_scale(self.x32) if kind == "fp8" else np.float32(1.0)
+
+    def codes(self, idx=slice(None)):
+        if self.kind == "fp8":
+            return encode_with_scale(self.x32[idx], self.scale)
+        return bf16_encode(self.x32[idx])
 
     def __getitem__(self, idx):
-        c = self.codes[idx]
+        c = self.codes(idx)
         if self.kind == "fp8":
             return dequantize_fp8(c, self.scale)
         return bf16_decode(c)
@@ -153,28 +164,26 @@ class _Dequantized:
 
 def prefill_reference(q32, k32, v32, dtype: str, causal: bool = True, rows=None,
                       softmax_scale: float | None = None):
-    """The whole path on float32 inputs: quantize each tensor, then attend.
+    """The whole path on float32 inputs: the input step, then attention.
 
     dtype "fp8": per-tensor absmax e4m3fn codes and scales; "bf16": bf16 RNE.
-    Attention runs in float64 on the dequantized values. With ``rows`` given,
-    only those (b, h, i) rows are computed. Returns a dict with the codes
-    (uint8 for fp8, uint16 bit patterns for bf16), the scales (1.0 for bf16),
-    and either the full O/LSE or the selected rows.
+    Attention runs in float64 on the dequantized values. Without ``rows``:
+    returns the codes (uint8 for fp8, uint16 bit patterns for bf16), the
+    scales (1.0 for bf16) and the full O / LSE. With ``rows`` (a list of
+    (b, h, i)): only those rows are computed (o_rows, lse_rows), together with
+    the scales; codes are then available per slice through ``views``.
     """
-    out = {}
-    if dtype == "fp8":
-        (qc, qs), (kc, ks), (vc, vs) = (quantize_fp8_per_tensor(t) for t in (q32, k32, v32))
-        views = [_Dequantized(qc, qs), _Dequantized(kc, ks), _Dequantized(vc, vs)]
-    elif dtype == "bf16":
-        qc, kc, vc = (bf16_encode(t) for t in (q32, k32, v32))
-        qs = ks = vs = np.float32(1.0)
-        views = [_Dequantized(qc, kind="bf16"), _Dequantized(kc, kind="bf16"),
-                 _Dequantized(vc, kind="bf16")]
-    else:
+    if dtype not in ("fp8", "bf16"):
         raise ValueError("dtype must be 'fp8' or 'bf16'")
-    out.update(q_codes=qc, k_codes=kc, v_codes=vc, q_scale=qs, k_scale=ks, v_scale=vs)
+    views = [_QuantizedView(t, dtype) for t in (q32, k32, v32)]
+    out = dict(q_scale=views[0].scale, k_scale=views[1].scale, v_scale=views[2].scale, views=views)
     if rows is None:
-        qd, kd, vd = (vw[:] for vw in views)
+        qc, kc, vc = (vw.codes() for vw in views)
+        out.update(q_codes=qc, k_codes=kc, v_codes=vc)
+        if dtype == "fp8":
+            qd, kd, vd = (dequantize_fp8(c, vw.scale) for c, vw in zip((qc, kc, vc), views))
+        else:
+            qd, kd, vd = (bf16_decode(c) for c in (qc, kc, vc))
         O, L = causal_attention(qd, kd, vd, causal=causal, softmax_scale=softmax_scale)
         out.update(o=O, lse=L)
     else:

@@ -91,13 +91,24 @@ def quantize_fp8_per_tensor(x: np.ndarray) -> tuple[np.ndarray, np.float32]:
     x ~= decode(codes) * scale.
     """
     x = np.asarray(x, dtype=np.float32)
+    scale = per_tensor_scale(x)
+    return encode_with_scale(x, scale), scale
+
+
+def per_tensor_scale(x: np.ndarray) -> np.float32:
+    """absmax(|x|) / 448 in fp32 (1.0 for an all-zero tensor)."""
+    x = np.asarray(x, dtype=np.float32)
     amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
     if amax == 0:
-        scale = np.float32(1.0)
-    else:
-        scale = np.float32(amax / np.float32(E4M3_MAX))
-    y = (x / scale).astype(np.float32)
-    return e4m3fn_encode(y), scale
+        return np.float32(1.0)
+    return np.float32(amax / np.float32(E4M3_MAX))
+
+
+def encode_with_scale(x: np.ndarray, scale) -> np.ndarray:
+    """e4m3fn codes of x / scale (fp32 division, then round to nearest even)."""
+    x = np.asarray(x, dtype=np.float32)
+    y = (x / np.float32(scale)).astype(np.float32)
+    return e4m3fn_encode(y)
 
 
 def dequantize_fp8(codes: np.ndarray, scale) -> np.ndarray:
