@@ -108,17 +108,23 @@ __device__ __forceinline__ void decode_work(const FwdParams& p, int& b, int& h, 
   }
 }
 
+// Per-lane partial row sums above this trigger the exact-maximum path (see
+// the softmax comment in the kernel). It keeps every probability <= 256,
+// inside the e4m3 range (448), and far from fp32 overflow.
+constexpr float kLazyMaxThreshold = 256.f;
+
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   ATTN_LDS char* smem = (ATTN_LDS char*)smem_raw;
 
-  constexpr int BM = C::BM, BN = C::BN, DQK = C::DQK, DV = C::DV;
+  constexpr int BM = C::BM, BN = C::BN, DV = C::DV;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int l32 = lane & 31;   // query column / operand row of this lane
   const int g = lane >> 5;     // contraction half
+  const int hh = lane >> 4, kk = lane & 15;
 
   int b, h, mt;
   decode_work<C>(p, b, h, mt);
@@ -137,8 +143,8 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   const float c_log2 = qs * ks * p.sm_scale * 1.4426950408889634f;
 
   const int64_t q_row_stride = (int64_t)p.Hq * C::KROW;
-  const int64_t kv_row_stride_k = (int64_t)p.Hkv * C::KROW;
-  const int64_t kv_row_stride_v = (int64_t)p.Hkv * C::VROW;
+  const int64_t k_row_stride = (int64_t)p.Hkv * C::KROW;
+  const int64_t v_row_stride = (int64_t)p.Hkv * C::VROW;
   const uint8_t* kbase = p.k + ((int64_t)b * S * p.Hkv + kvh) * C::KROW;
   const uint8_t* vbase = p.v + ((int64_t)b * S * p.Hkv + kvh) * C::VROW;
 
@@ -147,87 +153,99 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   constexpr int QREGS = C::FP8 ? 8 : 4;  // ints per k-step
   i32x4 qf[C::QK_STEPS * QREGS / 4];
   {
-    const uint8_t* qp = p.q + ((int64_t)b * S + qrow) * q_row_stride + (int64_t)h * C::KROW;
+    const uint8_t* qp = p.q + ((int64_t)b * S + min(qrow, S - 1)) * q_row_stride + (int64_t)h * C::KROW;
 #pragma unroll
     for (int u = 0; u < C::QK_STEPS; ++u) {
       if constexpr (C::FP8) {
         // bytes [64u + 32g, +32): chunks 4u + 2g, 4u + 2g + 1
         const int off = 64 * u + 32 * g;
-        i32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-        if (qrow < S) {
-          a = *(const i32x4*)(qp + off);
-          c = *(const i32x4*)(qp + off + 16);
-        }
-        qf[2 * u] = a;
-        qf[2 * u + 1] = c;
+        qf[2 * u] = *(const i32x4*)(qp + off);
+        qf[2 * u + 1] = *(const i32x4*)(qp + off + 16);
       } else {
         // elements [16u + 8g, +8) = bytes [32u + 16g, +16)
-        const int off = 32 * u + 16 * g;
-        i32x4 a = {0, 0, 0, 0};
-        if (qrow < S) a = *(const i32x4*)(qp + off);
-        qf[u] = a;
+        qf[u] = *(const i32x4*)(qp + 32 * u + 16 * g);
       }
     }
   }
 
-  // ---- key range
+  // ---- key range: causal tile skip
   const int n_kv = p.causal ? min(S, m0 + BM) : S;
   const int nblk = (n_kv + BN - 1) / BN;
 
-  // ---- staging of one K/V tile: global -> registers -> LDS
-  i32x4 kst[C::KLOADS], vst[C::VLOADS];
-  auto stage_load = [&](int n0) {
-#pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      const int cid = tid + i * C::NTHREADS;
-      const int row = cid / C::KCH, ch = cid % C::KCH;
-      const int key = n0 + row;
-      i32x4 x = {0, 0, 0, 0};
-      if (key < S) x = *(const i32x4*)(kbase + (int64_t)key * kv_row_stride_k + 16 * ch);
-      kst[i] = x;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VLOADS; ++i) {
-      const int cid = tid + i * C::NTHREADS;
-      const int row = cid / C::VCH, ch = cid % C::VCH;
-      const int key = n0 + row;
-      i32x4 x = {0, 0, 0, 0};
-      if (key < S) x = *(const i32x4*)(vbase + (int64_t)key * kv_row_stride_v + 16 * ch);
-      vst[i] = x;
-    }
-  };
-  auto stage_store = [&](int buf) {
+  // ---- HBM -> LDS staging of one K/V tile, straight into the swizzled LDS
+  // layout: instruction i of wave w fills LDS bytes [(i*NWAVES + w)*1024, +1024);
+  // lane l's 16 bytes are physical chunk (o % ROW)/16 of row o / ROW, so it
+  // loads the logical chunk that the swizzle maps there. Keys past the end
+  // are clamped to the last row (they are masked before use).
+  auto issue_tile = [&](int n0, int buf) {
     ATTN_LDS char* kl = smem + buf * C::STAGE;
     ATTN_LDS char* vl = kl + C::KTILE;
 #pragma unroll
     for (int i = 0; i < C::KLOADS; ++i) {
-      const int cid = tid + i * C::NTHREADS;
-      const int row = cid / C::KCH, ch = cid % C::KCH;
-      lds_write_b128(kl + row * C::KROW + 16 * swz<C::KCH>(ch, row), kst[i]);
+      const int blk = (i * C::NWAVES + wave) * 1024;
+      const int o = blk + 16 * lane;
+      const int row = o / C::KROW, ph = (o % C::KROW) / 16;
+      const int key = min(n0 + row, S - 1);
+      global_to_lds_16(kbase + (int64_t)key * k_row_stride + 16 * swz<C::KCH>(ph, row), kl + blk);
     }
 #pragma unroll
     for (int i = 0; i < C::VLOADS; ++i) {
-      const int cid = tid + i * C::NTHREADS;
-      const int row = cid / C::VCH, ch = cid % C::VCH;
-      lds_write_b128(vl + row * C::VROW + 16 * swz<C::VCH>(ch, row), vst[i]);
+      const int blk = (i * C::NWAVES + wave) * 1024;
+      const int o = blk + 16 * lane;
+      const int row = o / C::VROW, ph = (o % C::VROW) / 16;
+      const int key = min(n0 + row, S - 1);
+      global_to_lds_16(vbase + (int64_t)key * v_row_stride + 16 * swz<C::VCH>(ph, row), vl + blk);
     }
   };
+
+  // ---- per-lane LDS read offsets (the swizzle term depends on row & 7 only,
+  // which is fixed per lane for every tile below)
+  // K (A operand): row 32t + l32, chunk pair of contraction step u
+  int k_off[C::QK_STEPS][C::FP8 ? 2 : 1];
+#pragma unroll
+  for (int u = 0; u < C::QK_STEPS; ++u) {
+    if constexpr (C::FP8) {
+      k_off[u][0] = l32 * C::KROW + 16 * swz<C::KCH>(4 * u + 2 * g, l32);
+      k_off[u][1] = l32 * C::KROW + 16 * swz<C::KCH>(4 * u + 2 * g + 1, l32);
+    } else {
+      k_off[u][0] = l32 * C::KROW + 16 * swz<C::KCH>(2 * u + g, l32);
+    }
+  }
+  // V (A operand of O^T = V^T.P^T) through transpose reads. FP8: lane (dv row,
+  // half g) byte j holds key 64u + 32(j/16) + 8((j%16)/4) + 4g + j%4, the key
+  // that byte j of the P operand holds; the 16-lane group's 8 rows per read
+  // are keys base + {0..3, 8..11}. BF16: element e holds key
+  // 32t + 16cc + 8(e/4) + 4g + e%4, rows base + {0..3}.
+  int v_off[C::NOT];
+  {
+    const int krow_lane = C::FP8 ? (4 * (hh >> 1) + 8 * ((kk >> 1) >> 2) + ((kk >> 1) & 3))
+                                 : (4 * (hh >> 1) + (kk >> 2));
+#pragma unroll
+    for (int tv = 0; tv < C::NOT; ++tv) {
+      const int dv0 = 32 * tv + 16 * (hh & 1);
+      const int ch = C::FP8 ? dv0 / 16 : dv0 / 8 + ((kk & 3) >> 1);
+      v_off[tv] = krow_lane * C::VROW + 16 * swz<C::VCH>(ch, krow_lane) + 8 * (kk & 1);
+    }
+  }
 
   // ---- running state
   f32x16 oacc[C::NOT];
 #pragma unroll
   for (int t = 0; t < C::NOT; ++t) oacc[t] = f32x16{};
-  float m_run = -INFINITY;  // running max of t (log2 units)
-  float l_run = 0.f;        // this lane's share of the running row sum
+  // Running max of t (log2 units). Starting from a huge finite negative (not
+  // -inf) keeps fma(s, c, -m) free of inf - inf; the first tile always takes
+  // the exact path because its sums overflow the threshold.
+  float m_run = -1e30f;
+  float l_run = 0.f;  // this lane's share of the running row sum
 
-  stage_load(0);
-  stage_store(0);
+  issue_tile(0, 0);
+  wait_vmcnt0();
   __syncthreads();
 
   for (int n = 0; n < nblk; ++n) {
     const int n0 = n * BN;
     const bool more = n + 1 < nblk;
-    if (more) stage_load(n0 + BN);
+    if (more) issue_tile(n0 + BN, (n + 1) & 1);
 
     const ATTN_LDS char* kl = smem + (n & 1) * C::STAGE;
     const ATTN_LDS char* vl = kl + C::KTILE;
@@ -237,27 +255,24 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int t = 0; t < C::NST; ++t) {
       s[t] = f32x16{};
-      const int row = 32 * t + l32;
-      const ATTN_LDS char* kr = kl + row * C::KROW;
+      const ATTN_LDS char* kr = kl + 32 * t * C::KROW;
 #pragma unroll
       for (int u = 0; u < C::QK_STEPS; ++u) {
         if constexpr (C::FP8) {
-          const int c0 = 4 * u + 2 * g;
-          i32x4 a0 = lds_read_b128(kr + 16 * swz<C::KCH>(c0, row));
-          i32x4 a1 = lds_read_b128(kr + 16 * swz<C::KCH>(c0 + 1, row));
+          i32x4 a0 = lds_read_b128(kr + k_off[u][0]);
+          i32x4 a1 = lds_read_b128(kr + k_off[u][1]);
           i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
           i32x8 bq = {qf[2 * u][0], qf[2 * u][1], qf[2 * u][2], qf[2 * u][3],
                       qf[2 * u + 1][0], qf[2 * u + 1][1], qf[2 * u + 1][2], qf[2 * u + 1][3]};
           s[t] = mfma_f8(a, bq, s[t]);
         } else {
-          const int c0 = 2 * u + g;
-          i32x4 a = lds_read_b128(kr + 16 * swz<C::KCH>(c0, row));
+          i32x4 a = lds_read_b128(kr + k_off[u][0]);
           s[t] = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[u]), s[t]);
         }
       }
     }
 
-    // ---- mask (only tiles that cross the diagonal or the sequence end)
+    // ---- mask (wave-uniform branch: only tiles that cross the diagonal or the end)
     const bool need_mask = p.causal ? (n0 + BN - 1 > m0 + wave * 32) : (n0 + BN > S);
     if (need_mask) {
 #pragma unroll
@@ -271,94 +286,111 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
       }
     }
 
-    // ---- online softmax (exact exp2), log2 domain
-    float mx = -INFINITY;
+    // ---- online softmax, log2 domain, exact exp2.
+    // Probabilities are taken against the running max m_run as it stands
+    // (p = 2^(c*s - m_run)); the row max is only recomputed when some lane's
+    // partial sum of this tile exceeds the threshold, i.e. when the scores
+    // have grown well past m_run (always on the first tile). Every p then
+    // stays <= 256, and the result is the same softmax: m only shifts the
+    // common factor that O and l share.
+    float lsum;
+    i32x4 pf[C::FP8 ? BN / 32 * 2 : 1];     // FP8 P operand: 32 bytes per 64 keys
+    bf16x8 pb[C::FP8 ? 1 : C::NST * 2];     // BF16 P operand: 8 keys per lane-half per 16 keys
+    auto probs = [&](float m) {
+      lsum = 0.f;
+      if constexpr (C::FP8) {
 #pragma unroll
-    for (int t = 0; t < C::NST; ++t)
+        for (int u = 0; u < BN / 64; ++u) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * c_log2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    float lsum = 0.f;
+          for (int w = 0; w < 8; ++w) {
+            // byte j of the operand <- score tile 2u + j/16, register j%16
+            const int t = 2 * u + (w >> 2), r = 4 * (w & 3);
+            const float p0 = fast_exp2(__builtin_fmaf(s[t][r], c_log2, -m));
+            const float p1 = fast_exp2(__builtin_fmaf(s[t][r + 1], c_log2, -m));
+            const float p2 = fast_exp2(__builtin_fmaf(s[t][r + 2], c_log2, -m));
+            const float p3 = fast_exp2(__builtin_fmaf(s[t][r + 3], c_log2, -m));
+            lsum += (p0 + p1) + (p2 + p3);
+            const int x = cvt_fp8x2(p0, p1, 0, false);
+            pf[2 * u + (w >> 2)][w & 3] = cvt_fp8x2(p2, p3, x, true);
+          }
+        }
+      } else {
 #pragma unroll
-    for (int t = 0; t < C::NST; ++t)
+        for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(__builtin_fmaf(s[t][r], c_log2, -m_new));
-        s[t][r] = pv;
-        lsum += pv;
+          for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pv = fast_exp2(__builtin_fmaf(s[t][8 * cc + e], c_log2, -m));
+              lsum += pv;
+              pb[2 * t + cc][e] = (__bf16)pv;
+            }
+          }
+        }
       }
-    l_run = l_run * alpha + lsum;
+    };
+    probs(m_run);
+    if (wave_any(!(lsum <= kLazyMaxThreshold))) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
+      for (int t = 0; t < C::NST; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[t][r], s[t][r + 1]));
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m_run, mx * c_log2);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
+      probs(m_run);
+    }
+    l_run += lsum;
 
     // ---- O^T += V^T . P^T
     if constexpr (C::FP8) {
 #pragma unroll
       for (int u = 0; u < BN / 64; ++u) {
-        // B operand byte j <- score tile 2u + j/16, register j%16
-        i32x8 pf;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int t = 2 * u + (w >> 2), r = 4 * (w & 3);
-          int x = cvt_fp8x2(s[t][r], s[t][r + 1], 0, false);
-          pf[w] = cvt_fp8x2(s[t][r + 2], s[t][r + 3], x, true);
-        }
-        // V^T operand: lane (dv row l32, half g) byte j must hold the key that
-        // byte j of the P operand holds: key 64u + 32(j/16) + 8((j%16)/4) + 4g + j%4.
-        const int hh = lane >> 4, kk = lane & 15;
-        const int krow_lane = 4 * (hh >> 1) + 8 * ((kk >> 1) >> 2) + ((kk >> 1) & 3);
+        i32x8 pop = {pf[2 * u][0], pf[2 * u][1], pf[2 * u][2], pf[2 * u][3],
+                     pf[2 * u + 1][0], pf[2 * u + 1][1], pf[2 * u + 1][2], pf[2 * u + 1][3]};
 #pragma unroll
         for (int tv = 0; tv < C::NOT; ++tv) {
-          const int ch = 2 * tv + (hh & 1);
           i32x8 va;
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const int key = 64 * u + 32 * (rr >> 1) + 16 * (rr & 1) + krow_lane;
-            const ATTN_LDS char* ap = vl + key * C::VROW + 16 * swz<C::VCH>(ch, key) + 8 * (kk & 1);
-            i32x2 x = lds_read_tr8(ap);
+            const int key0 = 64 * u + 32 * (rr >> 1) + 16 * (rr & 1);
+            i32x2 x = lds_read_tr8(vl + key0 * C::VROW + v_off[tv]);
             va[2 * rr] = x[0];
             va[2 * rr + 1] = x[1];
           }
-          oacc[tv] = mfma_f8(va, pf, oacc[tv]);
+          oacc[tv] = mfma_f8(va, pop, oacc[tv]);
         }
       }
     } else {
-      const int hh = lane >> 4, kk = lane & 15;
 #pragma unroll
       for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          // B operand element e <- score tile t, register 8cc + e
-          bf16x8 pb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[t][8 * cc + e];
 #pragma unroll
           for (int tv = 0; tv < C::NOT; ++tv) {
-            // element e of lane (dv row, half g) <- key 32t + 16cc + 8(e/4) + 4g + e%4
-            const int dv0 = 32 * tv + 16 * (hh & 1);
-            const int chunk = dv0 / 8 + ((kk & 3) >> 1);
             i16x4 x[2];
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
-              const int key = 32 * t + 16 * cc + 8 * hp + 4 * (hh >> 1) + (kk >> 2);
-              const ATTN_LDS char* ap = vl + key * C::VROW + 16 * swz<C::VCH>(chunk, key) + 8 * (kk & 1);
-              x[hp] = lds_read_tr16(ap);
+              const int key0 = 32 * t + 16 * cc + 8 * hp;
+              x[hp] = lds_read_tr16(vl + key0 * C::VROW + v_off[tv]);
             }
-            i32x4 vi = {0, 0, 0, 0};
+            i32x4 vi;
             vi[0] = (int)(uint16_t)x[0][0] | ((int)(uint16_t)x[0][1] << 16);
             vi[1] = (int)(uint16_t)x[0][2] | ((int)(uint16_t)x[0][3] << 16);
             vi[2] = (int)(uint16_t)x[1][0] | ((int)(uint16_t)x[1][1] << 16);
             vi[3] = (int)(uint16_t)x[1][2] | ((int)(uint16_t)x[1][3] << 16);
-            oacc[tv] = mfma_bf16(__builtin_bit_cast(bf16x8, vi), pb, oacc[tv]);
+            oacc[tv] = mfma_bf16(__builtin_bit_cast(bf16x8, vi), pb[2 * t + cc], oacc[tv]);
           }
         }
       }
     }
 
-    if (more) stage_store((n + 1) & 1);
+    wait_vmcnt0();
     __syncthreads();
   }
 

@@ -70,4 +70,22 @@ __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old, bool hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16*l (lds_base must be wave-uniform; established on
+// hardware). Completion is tracked by vmcnt.
+#define ATTN_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ void global_to_lds_16(const void* gptr, ATTN_LDS char* lds_base) {
+  __builtin_amdgcn_global_load_lds((const ATTN_GLOBAL void*)gptr, (ATTN_LDS void*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): every
+// global load of this wave, including global-to-LDS loads, has completed.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wave-uniform value in a scalar register.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// True if any lane of the wave has `pred` set.
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
 }  // namespace attn
