@@ -1,0 +1,267 @@
+"""Throughput of the causal prefill attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole path over one batch of synthetic inputs
+that already sit in HBM: the input step (per-tensor FP8 quantization of Q, K
+and V, or the BF16 cast) and then the attention kernel (causal tile walk,
+Q.K^T, online softmax, P.V, O and LSE epilogue). The default workload is the
+long-context headline shape: B=1, S=32768, H=32, d=128, causal, FP8 e4m3
+with per-tensor scales, Q, K, V ~ N(0, 1).
+
+Prints ONE JSON line. ``value`` is the algorithmic causal FLOP count
+B*Hq*S^2*(d_qk+d_v) divided by the measured time of a whole step, in TFLOP/s.
+The attention kernel alone is reported beside it and in ``roofline``, whose
+duration comes from HIP events recorded on the stream the kernel runs on.
+``cpu_baseline`` times the fp64 CPU oracle on one (batch, head) slice of the
+same workload (all S query rows of head 0), on this host's cores.
+
+Only one GPU is used: ``--gpus`` above 1 exits with an error.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+HBM_GBS = 8000.0
+METRIC = "causal prefill attention TFLOP/s (FP8, d=128, S=32K) and % of dense FP8 MFMA peak"
+HEADLINE = "mha_fp8_32k"
+KERNEL_SOURCES = ["attn_fwd_kernel.h", "common.h", "api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bf16_causal_prefill_fwd_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, src_hash: str):
+    """HBM bytes per attention launch from the committed PMC summary.
+
+    profiles/attn_fwd_<workload>_traffic.txt holds ``key: value`` lines written
+    from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) scaled by a plain
+    copy of known size. It only counts if it was taken on the current kernel
+    sources (same source hash); otherwise the traffic is unknown (None).
+    """
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(w) -> float:
+    """Q, K, V read once, O (bf16) and LSE (fp32) written once."""
+    eb = 1 if w.dtype == "fp8" else 2
+    qkv = w.B * w.S * (w.Hq * w.d_qk + w.Hkv * w.d_qk + w.Hkv * w.d_v) * eb
+    out = w.B * w.S * w.Hq * w.d_v * 2 + w.B * w.Hq * w.S * 4
+    return float(qkv + out)
+
+
+def cpu_baseline(w, q, k, v) -> dict:
+    """The fp64 oracle on one head slice (b=0, h=0, every query row)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import causal_attention, dequantize_fp8, encode_with_scale, per_tensor_scale, bf16_encode, \
+        bf16_decode
+
+    G = w.Hq // w.Hkv
+    t0 = time.perf_counter()
+    if w.dtype == "fp8":
+        scales = [per_tensor_scale(x) for x in (q, k, v)]
+        sl = [dequantize_fp8(encode_with_scale(x[:1, :, 0:1], s), s) for x, s in zip((q, k, v), scales)]
+    else:
+        sl = [bf16_decode(bf16_encode(x[:1, :, 0:1])) for x in (q, k, v)]
+    causal_attention(*sl, causal=w.causal)
+    dt = time.perf_counter() - t0
+    flops = float(w.S) ** 2 * (w.d_qk + w.d_v) if w.causal else 2.0 * float(w.S) ** 2 * (w.d_qk + w.d_v)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle (input step + exact softmax attention) on batch 0, query head 0 "
+                   f"(kv head 0 of G={G}), all {w.S} rows: 1/{w.B * w.Hq} of the workload, "
+                   f"{flops / 1e9:.1f} GFLOP in {dt:.2f} s; host os.cpu_count()={os.cpu_count()}"),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path has no multi-GPU mode", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from bf16_causal_prefill_fwd_amd import ops
+    from bf16_causal_prefill_fwd_amd.workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (none visible)", file=sys.stderr)
+        return 2
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"# workload {w.name}: generating inputs (seed {args.seed})", file=sys.stderr, flush=True)
+    q, k, v = make_inputs(w, seed=args.seed)
+    q32, k32, v32 = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+
+    # preallocated buffers: nothing is allocated inside the timed region
+    if w.dtype == "fp8":
+        codes = [torch.empty(t.shape, dtype=torch.uint8, device=dev) for t in (q32, k32, v32)]
+    else:
+        codes = [torch.empty(t.shape, dtype=torch.bfloat16, device=dev) for t in (q32, k32, v32)]
+    scales = torch.empty(3, dtype=torch.float32, device=dev)
+    o = torch.empty((w.B, w.S, w.Hq, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def input_step():
+        if w.dtype == "fp8":
+            for i, t in enumerate((q32, k32, v32)):
+                ops.attn_quantize_fp8(t, out=codes[i], scale=scales[i:i + 1], stream=stream)
+        else:
+            for i, t in enumerate((q32, k32, v32)):
+                ops.attn_cast_bf16(t, out=codes[i], stream=stream)
+
+    def attention():
+        if w.dtype == "fp8":
+            ops.attn_prefill_fwd(*codes, causal=w.causal, out=o, lse=lse, d_scales=scales, stream=stream)
+        else:
+            ops.attn_prefill_fwd(*codes, causal=w.causal, out=o, lse=lse, stream=stream)
+
+    n_ev = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    print(f"# warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        input_step()
+        attention()
+    torch.cuda.synchronize()
+
+    print(f"# timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        input_step()
+        ev[i][1].record(stream)
+        attention()
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(n_ev)]
+    inp_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(n_ev)]
+    attn_avg = float(np.mean(attn_ms))
+    flops = w.causal_flops if w.causal else 2.0 * w.causal_flops
+    value = flops / (step_ms * 1e-3) / 1e12
+    attn_tflops = flops / (attn_avg * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    assert torch.isfinite(lse).all().item(), "non-finite LSE"
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profile(w.name, src_hash)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "d_qk": w.d_qk,
+                   "d_v": w.d_v, "causal": w.causal, "dist": w.dist, "seed": args.seed,
+                   "step": "input step (quantize/cast Q,K,V) + attention"},
+        "attention_ms": round(attn_avg, 4),
+        "attention_ms_min": round(float(np.min(attn_ms)), 4),
+        "attention_ms_median": round(float(np.median(attn_ms)), 4),
+        "attention_tflops": round(attn_tflops, 2),
+        "attention_frac_of_peak": round(attn_tflops / peak, 4),
+        "input_step_ms": round(float(np.mean(inp_ms)), 4),
+        "wall_s_timed": round(wall, 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"attn_fwd_kernel ({w.dtype}, d_qk={w.d_qk}, d_v={w.d_v})",
+            "achieved": round(attn_tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / peak, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": algorithmic_bytes(w),
+            "kernel_source_sha256_16": src_hash,
+        },
+        "pages_context": {"tflops": 2672.0, "hardware": "MI355X", "note": "FP8 d=128 32K Gaussian, "
+                          "attention alone, batch and heads not stated on the pages"},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (fp64 oracle, one head slice)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
