@@ -11,10 +11,10 @@
 namespace attn {
 
 // Kernel variants: (dtype, d_qk, d_v) -> tile configuration.
-using CfgF8D128 = FwdCfg<true, 128, 128, 128, 128>;
-using CfgF8D192 = FwdCfg<true, 192, 128, 128, 64>;
-using CfgBFD128 = FwdCfg<false, 128, 128, 128, 64>;
-using CfgBFD192 = FwdCfg<false, 192, 128, 128, 64>;
+using CfgF8D128 = FwdCfg<true, 128, 128, 64, 4>;
+using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4>;
+using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4>;
+using CfgBFD192 = FwdCfg<false, 192, 128, 32, 4>;
 
 namespace {
 
@@ -22,14 +22,7 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 int g_dev_state[kMaxDevices];  // 0 unknown, 1 ready (gfx950), -1 unsupported
 
-template <class C>
-hipError_t prepare_kernel() {
-  return hipFuncSetAttribute((const void*)attn_fwd_kernel<C>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             C::LDS_BYTES);
-}
-
-// Once per device: confirm gfx950 and raise the dynamic LDS limit of every
-// attention variant to its tile size.
+// Once per device: confirm gfx950.
 int device_ready() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
@@ -43,9 +36,6 @@ int device_ready() {
     g_dev_state[dev] = -1;
     return ATTN_ERR_UNSUPPORTED;
   }
-  if (prepare_kernel<CfgF8D128>() != hipSuccess || prepare_kernel<CfgF8D192>() != hipSuccess ||
-      prepare_kernel<CfgBFD128>() != hipSuccess || prepare_kernel<CfgBFD192>() != hipSuccess)
-    return ATTN_ERR_HIP;
   g_dev_state[dev] = 1;
   return ATTN_OK;
 }
@@ -61,7 +51,7 @@ int launch_fwd(FwdParams prm, hipStream_t stream) {
   const int64_t items = (int64_t)prm.B * prm.Hq * prm.n_mtiles;
   if (items > 0x7FFFFFFF) return ATTN_ERR_INVALID;
   prm.xcd_remap = (units % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(attn_fwd_kernel<C>, dim3((unsigned)items), dim3(C::NTHREADS), C::LDS_BYTES, stream, prm);
+  hipLaunchKernelGGL(attn_fwd_kernel<C>, dim3((unsigned)items), dim3(C::NTHREADS), 0, stream, prm);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -4,12 +4,27 @@
 // basta da solo"; ai4bro.com, "Why is FP8 attention slow on MI355X?"): the
 // two products Q.K^T and P.V run on the matrix cores, the row softmax between
 // them runs on the vector ALU, tile by tile over the keys with a running row
-// maximum and row sum. This file is its MI355X design:
+// maximum and row sum; the vector work per tile is close to the matrix work,
+// so the two have to overlap. This file is its MI355X design:
 //
-//  * One workgroup owns BM = 32 * NWAVES query rows of one (batch, head);
-//    each wave owns 32 rows and keeps its Q fragment in registers.
-//  * Key/value tiles of BN rows are staged HBM -> registers -> LDS with
-//    coalesced 16-byte loads, double buffered (one barrier per tile).
+//  * One workgroup = 4 waves = 128 query rows of one (batch, head); each
+//    wave owns 32 rows and keeps its Q fragment in registers. Two workgroups
+//    share a CU, so each SIMD runs two independent waves.
+//  * Software pipeline inside each wave, one key tile of BN keys per step
+//    (64 for FP8, 32 for BF16): while the softmax of tile n runs on the vector ALU, the same wave
+//    issues the MFMAs of S^T = K.Q^T for tile n+1 and of O^T += V^T.P^T for
+//    tile n-1, interleaved with it in a fixed order, so both pipes stay busy
+//    without relying on another wave's phase (the pages overlap the two
+//    with a two-wave ping-pong: ai4bro.com, "How does ZYFA work?";
+//    aicronaca.it, "Perché l'FP8 non basta da solo"). The LDS reads of the
+//    MFMA operands run two MFMAs ahead.
+//  * Key/value tiles go from HBM straight into LDS with coalesced 16-byte
+//    global-to-LDS loads, into K and V rings of NSTAGE stages, issued
+//    NSTAGE-1 steps before use; every wave waits only for its own loads
+//    (vmcnt) before the barrier that publishes them, once per step.
+//  * LDS rows are XOR-swizzled per tile kind so that every K read
+//    (ds_read_b128, 16 lanes per LDS cycle) and every transposed V read
+//    (ds_read_b64_tr_b8/_b16, 32 lanes per cycle) touches each bank once.
 //  * S^T = K.Q^T is computed (K is the MFMA A operand), so each lane holds
 //    scores of a single query: the row max needs one half-wave swap and the
 //    row sum stays lane-local until the epilogue.
@@ -18,8 +33,11 @@
 //    to match, and V is read in that order with LDS transpose reads, so V
 //    stays row-major in LDS.
 //  * Causal tile skip: a workgroup walks only key tiles up to its diagonal;
-//    only tiles that straddle the diagonal (or the sequence end) are masked.
+//    tiles that straddle a wave's diagonal or the sequence end are masked
+//    (a tile wholly past a wave's rows is simply fully masked).
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -40,47 +58,104 @@ struct FwdParams {
   int xcd_remap;
 };
 
-template <bool FP8_, int DQK_, int DV_, int BM_, int BN_>
+template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_>
 struct FwdCfg {
   static constexpr bool FP8 = FP8_;
-  static constexpr int DQK = DQK_, DV = DV_, BM = BM_, BN = BN_;
-  static constexpr int EB = FP8 ? 1 : 2;             // bytes per element
-  static constexpr int NWAVES = BM / 32;
+  static constexpr int DQK = DQK_, DV = DV_, BN = BN_;
+  static constexpr int BM = 128;                     // query rows per workgroup
+  static constexpr int NWAVES = 4;
   static constexpr int NTHREADS = NWAVES * 64;
+  static constexpr int EB = FP8 ? 1 : 2;             // bytes per element
   static constexpr int KROW = DQK * EB;              // bytes per K row
   static constexpr int VROW = DV * EB;               // bytes per V row
   static constexpr int KCH = KROW / 16;              // 16-byte chunks per K row
   static constexpr int VCH = VROW / 16;
   static constexpr int KTILE = BN * KROW;
   static constexpr int VTILE = BN * VROW;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int NSTAGE = NSTAGE_;             // K ring and V ring depth
+  static constexpr int LDS_BYTES = NSTAGE * (KTILE + VTILE);
   static constexpr int NST = BN / 32;                // 32-key score tiles
   static constexpr int NOT = DV / 32;                // 32-wide output tiles
   static constexpr int QK_STEPS = FP8 ? DQK / 64 : DQK / 16;
-  static constexpr int KLOADS = KTILE / 16 / NTHREADS;
+  static constexpr int PV_STEPS = FP8 ? BN / 64 : BN / 16;   // key steps of one P.V output tile
+  static constexpr int NPV = NOT * PV_STEPS;                 // P.V MFMAs per step
+  static constexpr int NQK = NST * QK_STEPS;                 // Q.K^T MFMAs per step
+  static constexpr int KLOADS = KTILE / 16 / NTHREADS;       // 16-byte loads per lane per tile
   static constexpr int VLOADS = VTILE / 16 / NTHREADS;
-  static_assert(BM % 32 == 0 && BN % 64 == 0, "tile sizes");
+  // loads a wave may leave in flight at the end of a step
+  static constexpr int INFLIGHT = (NSTAGE - 2) * (KLOADS + VLOADS);
+  static_assert((FP8 ? BN == 64 : (BN == 32 || BN == 64)), "FP8: 64 keys per step (one P operand); BF16: 32 or 64");
   static_assert(DV % 32 == 0 && DQK % 64 == 0, "head dims");
   static_assert(KTILE % (16 * NTHREADS) == 0 && VTILE % (16 * NTHREADS) == 0, "staging split");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(NSTAGE >= 2 && INFLIGHT < 64, "ring depth / vmcnt range");
+  static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per CU");
 };
 
-// Physical 16-byte chunk of logical chunk c in LDS row `row` (rows hold nch
-// chunks). XOR-swizzling by the row spreads the column reads of consecutive
-// rows over different banks. Rows of 12 chunks (FP8 d=192) swizzle chunks
-// 0..7 and 8..11 separately so every chunk stays inside its row.
+// LDS swizzles: physical 16-byte chunk of logical chunk c in tile row r.
+// Each is a bijection on a row's chunks and its own inverse (the staging
+// loads use it to find which logical chunk lands in a physical slot), and it
+// depends on r mod 16 only (every K read starts at a row that is a multiple
+// of 32, every V read at a multiple of 16 (FP8) or 8 (BF16, whose V swizzle
+// depends on r mod 4), so a lane's swizzle term is the same for every tile).
+// The LDS serves 256 bytes per cycle: 16 lanes of a ds_read_b128, 32 lanes
+// of an 8-byte read. The forms below make those lane groups hit distinct
+// banks for the access patterns of this kernel (measured on MI355X: an
+// earlier c ^ (r & 7) form made K reads 1.8x and V reads 1.6x slower).
+//
+// K tile (ds_read_b128 by rows 32t + lane%32): with a 128-byte row pitch
+// rows r and r+1 share a 256-byte bank line, so the term must differ within
+// every run of 16 rows.
 template <int NCH>
-__device__ __forceinline__ int swz(int c, int row) {
-  if constexpr (NCH % 8 == 0) {
-    return c ^ (row & 7);
-  } else {
-    static_assert(NCH == 12, "row width");
-    return c < 8 ? (c ^ (row & 7)) : (8 + ((c - 8) ^ (row & 3)));
+__host__ __device__ constexpr int k_swz(int c, int r) {
+  if constexpr (NCH == 8) {          // FP8 d=128: 128-byte rows
+    return c ^ ((r >> 1) & 7);
+  } else if constexpr (NCH == 12) {  // FP8 d=192: 192-byte rows, chunk quads
+    return 4 * (c >> 2) + ((c & 3) ^ ((r >> 2) & 3));
+  } else if constexpr (NCH == 16) {  // BF16 d=128: 256-byte rows
+    return c ^ (r & 15);
+  } else {                           // BF16 d=192: 384-byte rows, chunk octets
+    static_assert(NCH == 24, "K row width");
+    return 8 * (c >> 3) + ((c & 7) ^ ((r >> 1) & 7));
   }
 }
 
-template <class C>
+// V tile (transposed reads: 8 keys x 16 bytes (FP8) or 4 keys x 32 bytes
+// (BF16) per 16-lane group, two groups per LDS cycle reading adjacent
+// chunks of the same keys).
+template <int NCH>
+__host__ __device__ constexpr int v_swz(int c, int r) {
+  if constexpr (NCH == 8) {          // FP8 d_v=128: keys {0-3, 8-11} (+4) per group
+    return c ^ (2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1));
+  } else {                           // BF16 d_v=128: 4 consecutive keys per group
+    static_assert(NCH == 16, "V row width");
+    return c ^ (4 * (r & 3));
+  }
+}
+
+template <class F>
+constexpr bool swizzle_ok(F f, int nch) {
+  for (int r = 0; r < 32; ++r) {
+    bool seen[32] = {};
+    for (int c = 0; c < nch; ++c) {
+      const int ph = f(c, r);
+      if (ph < 0 || ph >= nch || seen[ph]) return false;
+      seen[ph] = true;
+      if (f(ph, r) != c) return false;        // involution
+      if (f(c, r + 16) != ph) return false;   // period 16 in the row
+    }
+  }
+  return true;
+}
+static_assert(swizzle_ok([](int c, int r) { return k_swz<8>(c, r); }, 8) &&
+              swizzle_ok([](int c, int r) { return k_swz<12>(c, r); }, 12) &&
+              swizzle_ok([](int c, int r) { return k_swz<16>(c, r); }, 16) &&
+              swizzle_ok([](int c, int r) { return k_swz<24>(c, r); }, 24),
+              "K swizzles");
+static_assert(swizzle_ok([](int c, int r) { return v_swz<8>(c, r); }, 8) &&
+              swizzle_ok([](int c, int r) { return v_swz<16>(c, r); }, 16),
+              "V swizzles");
+
+// Workgroup -> (batch, query head, query tile).
 __device__ __forceinline__ void decode_work(const FwdParams& p, int& b, int& h, int& mt) {
   const int bid = blockIdx.x;
   const int G = p.Hq / p.Hkv;
@@ -115,10 +190,14 @@ constexpr float kLazyMaxThreshold = 256.f;
 
 template <class C>
 __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  ATTN_LDS char* smem = (ATTN_LDS char*)smem_raw;
+  __shared__ __attribute__((aligned(1024))) char k_ring[C::NSTAGE * C::KTILE];
+  __shared__ __attribute__((aligned(1024))) char v_ring[C::NSTAGE * C::VTILE];
+  const ATTN_LDS char* k_lds = (const ATTN_LDS char*)k_ring;
+  const ATTN_LDS char* v_lds = (const ATTN_LDS char*)v_ring;
+  const uint32_t k_lds_addr = lds_address(k_ring);
+  const uint32_t v_lds_addr = lds_address(v_ring);
 
-  constexpr int BM = C::BM, BN = C::BN, DV = C::DV;
+  constexpr int BN = C::BN, DV = C::DV, NS = C::NSTAGE;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -127,11 +206,13 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   const int hh = lane >> 4, kk = lane & 15;
 
   int b, h, mt;
-  decode_work<C>(p, b, h, mt);
+  decode_work(p, b, h, mt);
   const int G = p.Hq / p.Hkv;
   const int kvh = h / G;
   const int S = p.S;
-  const int m0 = mt * BM;
+  const int m0 = mt * C::BM;
+  const int r0 = m0 + 32 * wave;   // first row of this wave
+  const int qrow = r0 + l32;
 
   float qs = p.q_scale, ks = p.k_scale, vs = p.v_scale;
   if (p.d_scales) {
@@ -139,7 +220,7 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
     ks = p.d_scales[1];
     vs = p.d_scales[2];
   }
-  // scores in log2 units: t = c * (q8 . k8)
+  // scores in log2 units: t = c * (q . k)
   const float c_log2 = qs * ks * p.sm_scale * 1.4426950408889634f;
 
   const int64_t q_row_stride = (int64_t)p.Hq * C::KROW;
@@ -148,8 +229,11 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   const uint8_t* kbase = p.k + ((int64_t)b * S * p.Hkv + kvh) * C::KROW;
   const uint8_t* vbase = p.v + ((int64_t)b * S * p.Hkv + kvh) * C::VROW;
 
+  // ---- key tiles of the workgroup (every wave runs every step)
+  const int n_kv = p.causal ? min(S, m0 + C::BM) : S;
+  const int T = (n_kv + BN - 1) / BN;
+
   // ---- Q fragment (B operand of S^T = K.Q^T), loaded once per wave
-  const int qrow = m0 + wave * 32 + l32;
   constexpr int QREGS = C::FP8 ? 8 : 4;  // ints per k-step
   i32x4 qf[C::QK_STEPS * QREGS / 4];
   {
@@ -168,54 +252,79 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
     }
   }
 
-  // ---- key range: causal tile skip
-  const int n_kv = p.causal ? min(S, m0 + BM) : S;
-  const int nblk = (n_kv + BN - 1) / BN;
-
-  // ---- HBM -> LDS staging of one K/V tile, straight into the swizzled LDS
-  // layout: instruction i of wave w fills LDS bytes [(i*NWAVES + w)*1024, +1024);
+  // ---- HBM -> LDS staging of tile `n` into ring stage n % NSTAGE:
+  // instruction i of wave w fills stage bytes [(i*NWAVES + w)*1024, +1024);
   // lane l's 16 bytes are physical chunk (o % ROW)/16 of row o / ROW, so it
   // loads the logical chunk that the swizzle maps there. Keys past the end
-  // are clamped to the last row (they are masked before use).
-  auto issue_tile = [&](int n0, int buf) {
-    ATTN_LDS char* kl = smem + buf * C::STAGE;
-    ATTN_LDS char* vl = kl + C::KTILE;
+  // are clamped to the last row (they are masked before use), and a tile
+  // index past the workgroup's last tile loads that last tile again (into a
+  // stage no step reads any more), so every step issues the same number of
+  // loads and the vmcnt bookkeeping is a constant.
+  // A lane's row within its 1 KB block and its swizzled chunk depend only on
+  // the instruction, not on the tile, so each instruction's row offset and
+  // chunk byte offset are precomputed per lane; a tile adds a wave-uniform
+  // row offset. Only a tile that crosses the sequence end clamps per lane.
+  int k_lrow[C::KLOADS], k_lch[C::KLOADS], v_lrow[C::VLOADS], v_lch[C::VLOADS];
+  // byte offset of the lane's source in a tile (kept in registers for FP8;
+  // BF16, whose register budget is tighter, recomputes it per load)
+  int64_t k_loff[C::KLOADS], v_loff[C::VLOADS];
 #pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      const int blk = (i * C::NWAVES + wave) * 1024;
-      const int o = blk + 16 * lane;
-      const int row = o / C::KROW, ph = (o % C::KROW) / 16;
-      const int key = min(n0 + row, S - 1);
-      global_to_lds_16(kbase + (int64_t)key * k_row_stride + 16 * swz<C::KCH>(ph, row), kl + blk);
-    }
+  for (int i = 0; i < C::KLOADS; ++i) {
+    const int o = (i * C::NWAVES + wave) * 1024 + 16 * lane;
+    k_lrow[i] = o / C::KROW;
+    k_lch[i] = 16 * k_swz<C::KCH>((o % C::KROW) / 16, k_lrow[i]);
+    k_loff[i] = C::FP8 ? (int64_t)k_lrow[i] * k_row_stride + k_lch[i] : 0;
+  }
 #pragma unroll
-    for (int i = 0; i < C::VLOADS; ++i) {
-      const int blk = (i * C::NWAVES + wave) * 1024;
-      const int o = blk + 16 * lane;
-      const int row = o / C::VROW, ph = (o % C::VROW) / 16;
-      const int key = min(n0 + row, S - 1);
-      global_to_lds_16(vbase + (int64_t)key * v_row_stride + 16 * swz<C::VCH>(ph, row), vl + blk);
+  for (int i = 0; i < C::VLOADS; ++i) {
+    const int o = (i * C::NWAVES + wave) * 1024 + 16 * lane;
+    v_lrow[i] = o / C::VROW;
+    v_lch[i] = 16 * v_swz<C::VCH>((o % C::VROW) / 16, v_lrow[i]);
+    v_loff[i] = C::FP8 ? (int64_t)v_lrow[i] * v_row_stride + v_lch[i] : 0;
+  }
+  auto issue_tile = [&](const uint8_t* base, int64_t stride, const int* lrow, const int* lch, const int64_t* loff,
+                        int nloads, uint32_t dst, int n) {
+    const int nn = min(n, T - 1);
+    const uint8_t* tb = base + (int64_t)(nn * BN) * stride;
+    if ((nn + 1) * BN <= S) {
+#pragma unroll
+      for (int i = 0; i < nloads; ++i) {
+        const int64_t off = C::FP8 ? loff[i] : (int64_t)lrow[i] * stride + lch[i];
+        global_to_lds_16_async(tb + off, dst + (i * C::NWAVES + wave) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < nloads; ++i) {
+        const int key = min(nn * BN + lrow[i], S - 1);
+        global_to_lds_16_async(base + (int64_t)key * stride + lch[i], dst + (i * C::NWAVES + wave) * 1024);
+      }
     }
   };
+  auto issue_k = [&](int n) {
+    issue_tile(kbase, k_row_stride, k_lrow, k_lch, k_loff, C::KLOADS, k_lds_addr + (n % NS) * C::KTILE, n);
+  };
+  auto issue_v = [&](int n) {
+    issue_tile(vbase, v_row_stride, v_lrow, v_lch, v_loff, C::VLOADS, v_lds_addr + (n % NS) * C::VTILE, n);
+  };
 
-  // ---- per-lane LDS read offsets (the swizzle term depends on row & 7 only,
-  // which is fixed per lane for every tile below)
+  // ---- per-lane LDS read offsets within a stage (the swizzle term depends
+  // on row mod 16 only, which is fixed per lane for every tile below)
   // K (A operand): row 32t + l32, chunk pair of contraction step u
   int k_off[C::QK_STEPS][C::FP8 ? 2 : 1];
 #pragma unroll
   for (int u = 0; u < C::QK_STEPS; ++u) {
     if constexpr (C::FP8) {
-      k_off[u][0] = l32 * C::KROW + 16 * swz<C::KCH>(4 * u + 2 * g, l32);
-      k_off[u][1] = l32 * C::KROW + 16 * swz<C::KCH>(4 * u + 2 * g + 1, l32);
+      k_off[u][0] = l32 * C::KROW + 16 * k_swz<C::KCH>(4 * u + 2 * g, l32);
+      k_off[u][1] = l32 * C::KROW + 16 * k_swz<C::KCH>(4 * u + 2 * g + 1, l32);
     } else {
-      k_off[u][0] = l32 * C::KROW + 16 * swz<C::KCH>(2 * u + g, l32);
+      k_off[u][0] = l32 * C::KROW + 16 * k_swz<C::KCH>(2 * u + g, l32);
     }
   }
   // V (A operand of O^T = V^T.P^T) through transpose reads. FP8: lane (dv row,
   // half g) byte j holds key 64u + 32(j/16) + 8((j%16)/4) + 4g + j%4, the key
   // that byte j of the P operand holds; the 16-lane group's 8 rows per read
   // are keys base + {0..3, 8..11}. BF16: element e holds key
-  // 32t + 16cc + 8(e/4) + 4g + e%4, rows base + {0..3}.
+  // 16u + 8(e/4) + 4g + e%4, rows base + {0..3}.
   int v_off[C::NOT];
   {
     const int krow_lane = C::FP8 ? (4 * (hh >> 1) + 8 * ((kk >> 1) >> 2) + ((kk >> 1) & 3))
@@ -224,7 +333,7 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
     for (int tv = 0; tv < C::NOT; ++tv) {
       const int dv0 = 32 * tv + 16 * (hh & 1);
       const int ch = C::FP8 ? dv0 / 16 : dv0 / 8 + ((kk & 3) >> 1);
-      v_off[tv] = krow_lane * C::VROW + 16 * swz<C::VCH>(ch, krow_lane) + 8 * (kk & 1);
+      v_off[tv] = krow_lane * C::VROW + 16 * v_swz<C::VCH>(ch, krow_lane) + 8 * (kk & 1);
     }
   }
 
@@ -238,161 +347,239 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   float m_run = -1e30f;
   float l_run = 0.f;  // this lane's share of the running row sum
 
-  issue_tile(0, 0);
-  wait_vmcnt0();
-  __syncthreads();
-
-  for (int n = 0; n < nblk; ++n) {
-    const int n0 = n * BN;
-    const bool more = n + 1 < nblk;
-    if (more) issue_tile(n0 + BN, (n + 1) & 1);
-
-    const ATTN_LDS char* kl = smem + (n & 1) * C::STAGE;
-    const ATTN_LDS char* vl = kl + C::KTILE;
-
-    // ---- S^T = K . Q^T
-    f32x16 s[C::NST];
+  // Scores and P operands are double-buffered by tile parity: step n reads
+  // the scores of tile n from sbuf[n&1] and writes tile n+1's into
+  // sbuf[~n&1]; it reads the P operand of tile n-1 from pbuf[~n&1] and
+  // writes tile n's into pbuf[n&1]. The loop is unrolled by two so every
+  // index is a constant (no register copies between steps).
+  f32x16 sbuf[2][C::NST];
+  constexpr int PREGS = C::FP8 ? 2 : C::PV_STEPS;   // FP8: 2 x i32x4 per 64 keys; BF16: one bf16x8 per 16 keys
+  typedef typename std::conditional<C::FP8, i32x4, bf16x8>::type PVec;
+  PVec pbuf[2][PREGS];
 #pragma unroll
-    for (int t = 0; t < C::NST; ++t) {
-      s[t] = f32x16{};
-      const ATTN_LDS char* kr = kl + 32 * t * C::KROW;
+  for (int i = 0; i < PREGS; ++i) pbuf[1][i] = PVec{};
+
+  // ---- matrix work of one step, as a list of MFMA jobs: P.V jobs (tile n-1)
+  // then Q.K^T jobs (tile n+1).
+  typedef typename std::conditional<C::FP8, i32x8, i32x4>::type Frag;
+  auto frag_reads = [](int j) constexpr -> int {
+    return j < C::NPV ? (C::FP8 ? 4 : 2) : (C::FP8 ? 2 : 1);
+  };
+  // A operand of job j (tile bases: vl for P.V, kl for Q.K^T)
+  auto load_frag = [&](int j, const ATTN_LDS char* vl, const ATTN_LDS char* kl) -> Frag {
+    Frag a;
+    if (j < C::NPV) {
+      const int tv = j % C::NOT, u = j / C::NOT;
+      if constexpr (C::FP8) {
 #pragma unroll
-      for (int u = 0; u < C::QK_STEPS; ++u) {
-        if constexpr (C::FP8) {
-          i32x4 a0 = lds_read_b128(kr + k_off[u][0]);
-          i32x4 a1 = lds_read_b128(kr + k_off[u][1]);
-          i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          i32x8 bq = {qf[2 * u][0], qf[2 * u][1], qf[2 * u][2], qf[2 * u][3],
-                      qf[2 * u + 1][0], qf[2 * u + 1][1], qf[2 * u + 1][2], qf[2 * u + 1][3]};
-          s[t] = mfma_f8(a, bq, s[t]);
-        } else {
-          i32x4 a = lds_read_b128(kr + k_off[u][0]);
-          s[t] = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[u]), s[t]);
+        for (int rr = 0; rr < 4; ++rr) {
+          const int key0 = 64 * u + 32 * (rr >> 1) + 16 * (rr & 1);
+          i32x2 x = lds_read_tr8(vl + key0 * C::VROW + v_off[tv]);
+          a[2 * rr] = x[0];
+          a[2 * rr + 1] = x[1];
         }
+      } else {
+        i16x4 x[2];
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) x[hp] = lds_read_tr16(vl + (16 * u + 8 * hp) * C::VROW + v_off[tv]);
+        a[0] = (int)(uint16_t)x[0][0] | ((int)(uint16_t)x[0][1] << 16);
+        a[1] = (int)(uint16_t)x[0][2] | ((int)(uint16_t)x[0][3] << 16);
+        a[2] = (int)(uint16_t)x[1][0] | ((int)(uint16_t)x[1][1] << 16);
+        a[3] = (int)(uint16_t)x[1][2] | ((int)(uint16_t)x[1][3] << 16);
+      }
+    } else {
+      const int jq = j - C::NPV, t = jq / C::QK_STEPS, u = jq % C::QK_STEPS;
+      const ATTN_LDS char* kr = kl + 32 * t * C::KROW;
+      if constexpr (C::FP8) {
+        i32x4 a0 = lds_read_b128(kr + k_off[u][0]);
+        i32x4 a1 = lds_read_b128(kr + k_off[u][1]);
+        a = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      } else {
+        a = lds_read_b128(kr + k_off[u][0]);
       }
     }
+    return a;
+  };
+  // job j: P.V jobs accumulate into oacc with operand P = pbuf[PP]; Q.K^T
+  // jobs write the score tiles sbuf[SQ]
+  auto run_job = [&](int j, const Frag& a, auto PPc, auto SQc) {
+    constexpr int PP = decltype(PPc)::value, SQ = decltype(SQc)::value;
+    const PVec* pv = pbuf[PP];
+    f32x16* sq = sbuf[SQ];
+    if (j < C::NPV) {
+      const int tv = j % C::NOT, u = j / C::NOT;
+      if constexpr (C::FP8) {
+        i32x8 pop = {pv[0][0], pv[0][1], pv[0][2], pv[0][3], pv[1][0], pv[1][1], pv[1][2], pv[1][3]};
+        oacc[tv] = mfma_f8(a, pop, oacc[tv]);
+      } else {
+        oacc[tv] = mfma_bf16(__builtin_bit_cast(bf16x8, a), pv[u], oacc[tv]);
+      }
+    } else {
+      const int jq = j - C::NPV, t = jq / C::QK_STEPS, u = jq % C::QK_STEPS;
+      const f32x16 acc = u == 0 ? f32x16{} : sq[t];
+      if constexpr (C::FP8) {
+        i32x8 bq = {qf[2 * u][0], qf[2 * u][1], qf[2 * u][2], qf[2 * u][3],
+                    qf[2 * u + 1][0], qf[2 * u + 1][1], qf[2 * u + 1][2], qf[2 * u + 1][3]};
+        sq[t] = mfma_f8(a, bq, acc);
+      } else {
+        sq[t] = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[u]), acc);
+      }
+    }
+  };
 
-    // ---- mask (wave-uniform branch: only tiles that cross the diagonal or the end)
-    const bool need_mask = p.causal ? (n0 + BN - 1 > m0 + wave * 32) : (n0 + BN > S);
+  // ---- softmax of one tile, in NCHUNK chunks (interleaved with the MFMA
+  // jobs). Log2 domain, exact exp2, P rounded to the operand type.
+  // Probabilities are taken against the running max m_run as it stands
+  // (p = 2^(c*s - m_run)); the row max is only recomputed when some lane's
+  // partial sum of a tile exceeds the threshold, i.e. when the scores have
+  // grown well past m_run (always on the first tile). Every p then stays
+  // <= 256, and the result is the same softmax: m only shifts the common
+  // factor that O and l share.
+  constexpr int NCHUNK = C::NST * 4;              // 4 fp32 scores per lane each
+  auto probs_chunk = [&](int c, auto Pc, float m, float& lsum) {
+    constexpr int P = decltype(Pc)::value;
+    const f32x16* sc = sbuf[P];
+    PVec* pout = pbuf[P];
+    // chunk c: score tile t = c / 4, registers r .. r+3
+    const int t = c >> 2, r = 4 * (c & 3);
+    const float p0 = fast_exp2(__builtin_fmaf(sc[t][r], c_log2, -m));
+    const float p1 = fast_exp2(__builtin_fmaf(sc[t][r + 1], c_log2, -m));
+    const float p2 = fast_exp2(__builtin_fmaf(sc[t][r + 2], c_log2, -m));
+    const float p3 = fast_exp2(__builtin_fmaf(sc[t][r + 3], c_log2, -m));
+    lsum += (p0 + p1) + (p2 + p3);
+    if constexpr (C::FP8) {
+      // FP8 operand byte j <- score tile j/16, register j%16: chunk c fills
+      // dword (c & 3) of pout[t]
+      const int x = cvt_fp8x2(p0, p1, 0, false);
+      pout[t][c & 3] = pin(cvt_fp8x2(p2, p3, x, true));
+    } else {
+      // BF16 operand u = 2t + (r / 8) holds registers 8(u%2) .. +7 of tile t
+      const int u = 2 * t + (r >> 3), e = r & 7;
+      pout[u][e] = (__bf16)p0;
+      pout[u][e + 1] = (__bf16)p1;
+      pout[u][e + 2] = (__bf16)p2;
+      pout[u][e + 3] = (__bf16)p3;
+    }
+  };
+
+  // exact-maximum path for a tile whose partial sums overflowed: new row
+  // max, rescale of l and O (O holds every P.V issued so far), P again.
+  auto exact_path = [&](auto Pc, float& lsum) {
+    constexpr int P = decltype(Pc)::value;
+    const f32x16* sc = sbuf[P];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < C::NST; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[t][r], sc[t][r + 1]));
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx * c_log2);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
+    lsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NCHUNK; ++c) probs_chunk(c, Pc, m_run, lsum);
+  };
+
+  constexpr int NJOB = C::NPV + C::NQK;
+  // ---- one pipeline step n with parity P (tile n's scores in sbuf[P])
+  auto step = [&](int n, auto Pc) {
+    constexpr int P = decltype(Pc)::value, Q = 1 - P;
+    const int n0 = n * BN;
+    // mask (wave-uniform branch: tiles that straddle this wave's diagonal,
+    // lie wholly past its rows, or cross the sequence end)
+    const bool need_mask = p.causal ? (n0 + BN - 1 > r0) : (n0 + BN > S);
     if (need_mask) {
 #pragma unroll
       for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = n0 + 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool hidden = p.causal ? (key > qrow) : (key >= S);
-          if (hidden) s[t][r] = -INFINITY;
+          const bool hidden = p.causal ? (key > qrow || key >= S) : (key >= S);
+          sbuf[P][t][r] = hidden ? -INFINITY : sbuf[P][t][r];
         }
       }
     }
-
-    // ---- online softmax, log2 domain, exact exp2.
-    // Probabilities are taken against the running max m_run as it stands
-    // (p = 2^(c*s - m_run)); the row max is only recomputed when some lane's
-    // partial sum of this tile exceeds the threshold, i.e. when the scores
-    // have grown well past m_run (always on the first tile). Every p then
-    // stays <= 256, and the result is the same softmax: m only shifts the
-    // common factor that O and l share.
-    float lsum;
-    i32x4 pf[C::FP8 ? BN / 32 * 2 : 1];     // FP8 P operand: 32 bytes per 64 keys
-    bf16x8 pb[C::FP8 ? 1 : C::NST * 2];     // BF16 P operand: 8 keys per lane-half per 16 keys
-    auto probs = [&](float m) {
-      lsum = 0.f;
-      if constexpr (C::FP8) {
+    // V(n-1) sits in stage (n-1) % NS; at n = 0 P is zero and stage 0 (V(0)) is read
+    const ATTN_LDS char* vl = v_lds + (n == 0 ? 0 : (n - 1) % NS) * C::VTILE;
+    const ATTN_LDS char* kl = k_lds + ((n + 1) % NS) * C::KTILE;
+    // MFMA jobs interleaved with the softmax chunks of tile n; job j's LDS
+    // reads go out two jobs ahead (3-deep operand ring)
+    float lsum = 0.f;
+    Frag fr[3];
+    fr[0] = load_frag(0, vl, kl);
+    fr[1] = load_frag(1, vl, kl);
+    sched_group<kSchedDsRead>(frag_reads(0) + frag_reads(1));
+    int c = 0;
 #pragma unroll
-        for (int u = 0; u < BN / 64; ++u) {
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            // byte j of the operand <- score tile 2u + j/16, register j%16
-            const int t = 2 * u + (w >> 2), r = 4 * (w & 3);
-            const float p0 = fast_exp2(__builtin_fmaf(s[t][r], c_log2, -m));
-            const float p1 = fast_exp2(__builtin_fmaf(s[t][r + 1], c_log2, -m));
-            const float p2 = fast_exp2(__builtin_fmaf(s[t][r + 2], c_log2, -m));
-            const float p3 = fast_exp2(__builtin_fmaf(s[t][r + 3], c_log2, -m));
-            lsum += (p0 + p1) + (p2 + p3);
-            const int x = cvt_fp8x2(p0, p1, 0, false);
-            pf[2 * u + (w >> 2)][w & 3] = cvt_fp8x2(p2, p3, x, true);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < C::NST; ++t) {
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float pv = fast_exp2(__builtin_fmaf(s[t][8 * cc + e], c_log2, -m));
-              lsum += pv;
-              pb[2 * t + cc][e] = (__bf16)pv;
-            }
-          }
-        }
+    for (int j = 0; j < NJOB; ++j) {
+      if (j + 2 < NJOB) fr[(j + 2) % 3] = load_frag(j + 2, vl, kl);
+      run_job(j, fr[j % 3], std::integral_constant<int, Q>{}, std::integral_constant<int, Q>{});
+      // this step's loads (K(n+NS), V(n+NS-2)) go out behind the first MFMA,
+      // so their address arithmetic overlaps the softmax
+      if (j == 0) {
+        issue_k(n + NS);
+        issue_v(n + NS - 2);
       }
-    };
-    probs(m_run);
-    if (wave_any(!(lsum <= kLazyMaxThreshold))) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < C::NST; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[t][r], s[t][r + 1]));
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx * c_log2);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
-      probs(m_run);
+      // chunks are spread over all but the last two jobs, so the row-sum
+      // chain is complete (for the lazy-max check below) by the time the
+      // last MFMAs have issued
+      const int c_end = j + 2 >= NJOB ? NCHUNK : (j + 1) * NCHUNK / (NJOB - 2);
+      for (; c < c_end; ++c) probs_chunk(c, Pc, m_run, lsum);
+      // issue order: this job's look-ahead reads, then its MFMA; the softmax
+      // instructions are left to the scheduler (pinning them measured slower)
+      if (j + 2 < NJOB) sched_group<kSchedDsRead>(frag_reads(j + 2));
+      sched_group<kSchedMfma>(1);
     }
-    l_run += lsum;
-
-    // ---- O^T += V^T . P^T
-    if constexpr (C::FP8) {
-#pragma unroll
-      for (int u = 0; u < BN / 64; ++u) {
-        i32x8 pop = {pf[2 * u][0], pf[2 * u][1], pf[2 * u][2], pf[2 * u][3],
-                     pf[2 * u + 1][0], pf[2 * u + 1][1], pf[2 * u + 1][2], pf[2 * u + 1][3]};
-#pragma unroll
-        for (int tv = 0; tv < C::NOT; ++tv) {
-          i32x8 va;
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int key0 = 64 * u + 32 * (rr >> 1) + 16 * (rr & 1);
-            i32x2 x = lds_read_tr8(vl + key0 * C::VROW + v_off[tv]);
-            va[2 * rr] = x[0];
-            va[2 * rr + 1] = x[1];
-          }
-          oacc[tv] = mfma_f8(va, pop, oacc[tv]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < C::NST; ++t) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-          for (int tv = 0; tv < C::NOT; ++tv) {
-            i16x4 x[2];
-#pragma unroll
-            for (int hp = 0; hp < 2; ++hp) {
-              const int key0 = 32 * t + 16 * cc + 8 * hp;
-              x[hp] = lds_read_tr16(vl + key0 * C::VROW + v_off[tv]);
-            }
-            i32x4 vi;
-            vi[0] = (int)(uint16_t)x[0][0] | ((int)(uint16_t)x[0][1] << 16);
-            vi[1] = (int)(uint16_t)x[0][2] | ((int)(uint16_t)x[0][3] << 16);
-            vi[2] = (int)(uint16_t)x[1][0] | ((int)(uint16_t)x[1][1] << 16);
-            vi[3] = (int)(uint16_t)x[1][2] | ((int)(uint16_t)x[1][3] << 16);
-            oacc[tv] = mfma_bf16(__builtin_bit_cast(bf16x8, vi), pb[2 * t + cc], oacc[tv]);
-          }
-        }
-      }
-    }
-
-    wait_vmcnt0();
+    wait_vmcnt<C::INFLIGHT>();
     __syncthreads();
+    // lazy-max check of tile n after the barrier, by when its row sums are
+    // complete (the exact path touches registers only)
+    if (wave_any(!(lsum <= kLazyMaxThreshold))) exact_path(Pc, lsum);
+    l_run += lsum;
+  };
+
+  // ---- prologue: stages of K(0..NS-1) and V(0..NS-3) in flight, then all
+  // published; S^T of tile 0 into sbuf[0].
+#pragma unroll
+  for (int n = 0; n < NS; ++n) issue_k(n);
+#pragma unroll
+  for (int n = 0; n < NS - 2; ++n) issue_v(n);
+  wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int j = C::NPV; j < NJOB; ++j)
+    run_job(j, load_frag(j, v_lds, k_lds), std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  // step 0 loads K(NS) into stage 0, which every wave has just read
+  __syncthreads();
+
+  // ---- main loop. Step n: S^T of tile n+1 and O += P.V of tile n-1 on the
+  // matrix cores while the softmax of tile n runs; K(n+NS) and V(n+NS-2) are
+  // loaded meanwhile (their stages were last read in step n-1). At the end
+  // each wave waits for all but the last NS-2 steps' loads, so K(n+2) and
+  // V(n) are complete at the barrier.
+  for (int n = 0; n < T; n += 2) {
+    step(n, std::integral_constant<int, 0>{});
+    if (n + 1 >= T) break;
+    step(n + 1, std::integral_constant<int, 1>{});
   }
+  // last tile T-1: its lazy-max check, then its P.V (V stage complete: waited
+  // at the end of step T-2)
+  {
+    const ATTN_LDS char* vl = v_lds + ((T - 1) % NS) * C::VTILE;
+    auto finish = [&](auto Pc) {
+      constexpr int P = decltype(Pc)::value;
+#pragma unroll
+      for (int j = 0; j < C::NPV; ++j)
+        run_job(j, load_frag(j, vl, k_lds), Pc, std::integral_constant<int, 1 - P>{});
+    };
+    if ((T - 1) & 1) finish(std::integral_constant<int, 1>{});
+    else finish(std::integral_constant<int, 0>{});
+  }
+  wait_vmcnt<0>();  // drain the loads of the last steps before the workgroup ends
 
   // ---- epilogue: O = O_acc * v_scale / l, LSE = ln2 * (m + log2 l)
   const float l_tot = l_run + swap_halves(l_run);

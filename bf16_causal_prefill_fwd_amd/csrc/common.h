@@ -70,17 +70,76 @@ __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old, bool hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds_base + 16*l (lds_base must be wave-uniform; established on
-// hardware). Completion is tracked by vmcnt.
-#define ATTN_GLOBAL __attribute__((address_space(1)))
-__device__ __forceinline__ void global_to_lds_16(const void* gptr, ATTN_LDS char* lds_base) {
-  __builtin_amdgcn_global_load_lds((const ATTN_GLOBAL void*)gptr, (ATTN_LDS void*)lds_base, 16, 0, 0);
+// Byte address of an LDS object (what M0 and ds_* address operands hold).
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const ATTN_LDS void*)p;
 }
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): every
-// global load of this wave, including global-to-LDS loads, has completed.
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds_addr + 16*l (lds_addr is wave-uniform; the instruction takes
+// it from M0). Issued as inline assembly so that the compiler does not
+// treat later LDS reads of other ring stages as dependent on it: the caller
+// tracks completion itself with wait_vmcnt() before the barrier that
+// publishes the stage. M0 is set immediately before the load, with one
+// wait state, and this file uses no other construct that needs M0.
+__device__ __forceinline__ void global_to_lds_16_async(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left at their maxima): at most N
+// of this wave's vector memory loads, the youngest, are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // vmcnt bits [3:0] and [15:14]; expcnt (bits 6:4) and lgkmcnt (11:8) at max
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Compiler scheduling fence: no instruction is moved across it.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Scheduling groups: the next `n` instructions of the class (in the current
+// scheduling region) are placed here, in the order of these calls.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+// (n is a constant after unrolling; the builtin wants it literal.)
+template <int MASK>
+__device__ __forceinline__ void sched_group(int n) {
+  switch (n) {
+    case 1: __builtin_amdgcn_sched_group_barrier(MASK, 1, 0); break;
+    case 2: __builtin_amdgcn_sched_group_barrier(MASK, 2, 0); break;
+    case 3: __builtin_amdgcn_sched_group_barrier(MASK, 3, 0); break;
+    case 4: __builtin_amdgcn_sched_group_barrier(MASK, 4, 0); break;
+    case 5: __builtin_amdgcn_sched_group_barrier(MASK, 5, 0); break;
+    case 6: __builtin_amdgcn_sched_group_barrier(MASK, 6, 0); break;
+    case 7: __builtin_amdgcn_sched_group_barrier(MASK, 7, 0); break;
+    case 8: __builtin_amdgcn_sched_group_barrier(MASK, 8, 0); break;
+    case 12: __builtin_amdgcn_sched_group_barrier(MASK, 12, 0); break;
+    case 14: __builtin_amdgcn_sched_group_barrier(MASK, 14, 0); break;
+    case 16: __builtin_amdgcn_sched_group_barrier(MASK, 16, 0); break;
+    case 28: __builtin_amdgcn_sched_group_barrier(MASK, 28, 0); break;
+    case 32: __builtin_amdgcn_sched_group_barrier(MASK, 32, 0); break;
+    default: break;
+  }
+}
+
+// Materialises x at this point of the program (an empty asm that reads and
+// writes it): keeps the compiler from sinking its computation into a later
+// conditional block.
+__device__ __forceinline__ int pin(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Wave priority for instruction issue (0 = default).
+template <int P>
+__device__ __forceinline__ void set_priority() {
+  __builtin_amdgcn_s_setprio(P);
+}
 
 // Wave-uniform value in a scalar register.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
