@@ -22,6 +22,7 @@ Only one GPU is used: ``--gpus`` above 1 exits with an error.
 from __future__ import annotations
 
 import argparse
+import math
 import hashlib
 import json
 import os
@@ -85,13 +86,14 @@ def cpu_baseline(w, q, k, v) -> dict:
     """The fp64 oracle on one head slice (b=0, h=0, every query row)."""
     from threadpoolctl import threadpool_info
 
-    from oracle import causal_attention, dequantize_fp8, encode_with_scale, per_tensor_scale, bf16_encode, \
-        bf16_decode
+    from oracle import causal_attention, dequantize_fp8, encode_with_scale, per_tensor_scale, \
+        per_tensor_scale_folded, bf16_encode, bf16_decode
 
     G = w.Hq // w.Hkv
     t0 = time.perf_counter()
     if w.dtype == "fp8":
-        scales = [per_tensor_scale(x) for x in (q, k, v)]
+        ks, vs = per_tensor_scale(k), per_tensor_scale(v)
+        scales = [per_tensor_scale_folded(q, ks, 1.0 / math.sqrt(w.d_qk)), ks, vs]
         sl = [dequantize_fp8(encode_with_scale(x[:1, :, 0:1], s), s) for x, s in zip((q, k, v), scales)]
     else:
         sl = [bf16_decode(bf16_encode(x[:1, :, 0:1])) for x in (q, k, v)]
@@ -157,10 +159,15 @@ def main(argv=None) -> int:
     lse = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    sm_scale = 1.0 / math.sqrt(w.d_qk)
+
     def input_step():
         if w.dtype == "fp8":
-            for i, t in enumerate((q32, k32, v32)):
-                ops.attn_quantize_fp8(t, out=codes[i], scale=scales[i:i + 1], stream=stream)
+            # K and V first: the query's folded scale is derived from K's
+            for i in (1, 2):
+                ops.attn_quantize_fp8((q32, k32, v32)[i], out=codes[i], scale=scales[i:i + 1], stream=stream)
+            ops.attn_quantize_fp8(q32, out=codes[0], scale=scales[0:1], stream=stream, k_scale=scales[1:2],
+                                  softmax_scale=sm_scale)
         else:
             for i, t in enumerate((q32, k32, v32)):
                 ops.attn_cast_bf16(t, out=codes[i], stream=stream)

@@ -64,6 +64,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, f
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
   if (S > (1 << 24)) return ATTN_ERR_INVALID;
+  // a 64-key K or V tile spans 64 rows of Hkv * d bytes: its byte offsets
+  // must fit the staging loads' 32-bit offsets
+  if ((int64_t)Hkv * (d_qk > d_v ? d_qk : d_v) * 2 * 64 >= ((int64_t)1 << 31)) return ATTN_ERR_INVALID;
   if (!d_scales && !(good_scale(q_scale) && good_scale(k_scale) && good_scale(v_scale))) return ATTN_ERR_INVALID;
   if (!good_scale(softmax_scale)) return ATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
@@ -119,7 +122,10 @@ int attn_prefill_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
                         d_v, causal, dtype, stream);
 }
 
-int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, hipStream_t stream) {
+namespace {
+
+int quantize_impl(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, const float* d_k_scale,
+                  float softmax_scale, hipStream_t stream) {
   if (!x || !x8 || !d_scale) return ATTN_ERR_INVALID;
   if (n <= 0 || n >= ((int64_t)1 << 40)) return ATTN_ERR_INVALID;
   if (x_dtype != 0 && x_dtype != 1) return ATTN_ERR_UNSUPPORTED;
@@ -129,9 +135,29 @@ int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float*
   const char* sb = (const char*)d_scale;
   const char* ob = (const char*)x8;
   if ((sb + 4 > xb && sb < xe) || (sb + 4 > ob && sb < ob + n)) return ATTN_ERR_INVALID;
+  if (d_k_scale) {
+    if ((uintptr_t)d_k_scale & 3u) return ATTN_ERR_INVALID;
+    if (!(isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_ERR_INVALID;
+    const char* kb = (const char*)d_k_scale;
+    if (kb + 4 > sb && kb < sb + 4) return ATTN_ERR_INVALID;
+  }
   const int ready = attn::device_ready();
   if (ready != ATTN_OK) return ready;
-  return attn::launch_quantize_fp8(x, x_dtype, n, x8, d_scale, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return attn::launch_quantize_fp8(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, stream) == hipSuccess
+             ? ATTN_OK
+             : ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, hipStream_t stream) {
+  return quantize_impl(x, x_dtype, n, x8, d_scale, nullptr, 0.f, stream);
+}
+
+int attn_quantize_fp8_q(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, const float* d_k_scale,
+                        float softmax_scale, hipStream_t stream) {
+  if (!d_k_scale) return ATTN_ERR_INVALID;
+  return quantize_impl(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, stream);
 }
 
 int attn_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream) {

@@ -73,6 +73,8 @@ struct FwdCfg {
   static constexpr int KTILE = BN * KROW;
   static constexpr int VTILE = BN * VROW;
   static constexpr int NSTAGE = NSTAGE_;             // K ring and V ring depth
+  // folded score form available (the scaled MFMA exists for FP8 only)
+  static constexpr bool FOLDABLE = FP8;
   static constexpr int LDS_BYTES = NSTAGE * (KTILE + VTILE);
   static constexpr int NST = BN / 32;                // 32-key score tiles
   static constexpr int NOT = DV / 32;                // 32-wide output tiles
@@ -188,14 +190,25 @@ __device__ __forceinline__ void decode_work(const FwdParams& p, int& b, int& h, 
 // inside the e4m3 range (448), and far from fp32 overflow.
 constexpr float kLazyMaxThreshold = 256.f;
 
-template <class C>
-__global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char k_ring[C::NSTAGE * C::KTILE];
-  __shared__ __attribute__((aligned(1024))) char v_ring[C::NSTAGE * C::VTILE];
+// Scores as the MFMA hands them to the softmax. In both forms the softmax
+// works on t = c * (q . k) - m in log2 units, with c = q_scale * k_scale *
+// softmax_scale * log2(e) and m the running row maximum.
+//  * kScaleFma: the MFMA gives q . k; one fma per score forms t.
+//  * kScaleFolded (FP8, when c is a power of two 2^kc): the MFMA applies 2^kc
+//    through its E8M0 operand scales and starts its accumulation from -m, so
+//    it hands over t itself and the fma disappears from the softmax. The
+//    input step can pick Q's per-tensor scale so that c is a power of two.
+enum ScoreForm { kScaleFma = 0, kScaleFolded = 1 };
+
+template <class C, int FORM>
+__device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, char* v_ring, float vs,
+                                              float c_log2, int kc) {
   const ATTN_LDS char* k_lds = (const ATTN_LDS char*)k_ring;
   const ATTN_LDS char* v_lds = (const ATTN_LDS char*)v_ring;
   const uint32_t k_lds_addr = lds_address(k_ring);
   const uint32_t v_lds_addr = lds_address(v_ring);
+  constexpr bool FOLD = FORM == kScaleFolded;
+  static_assert(!FOLD || C::FP8, "scale folding needs the scaled FP8 MFMA");
 
   constexpr int BN = C::BN, DV = C::DV, NS = C::NSTAGE;
   const int tid = threadIdx.x;
@@ -214,14 +227,10 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   const int r0 = m0 + 32 * wave;   // first row of this wave
   const int qrow = r0 + l32;
 
-  float qs = p.q_scale, ks = p.k_scale, vs = p.v_scale;
-  if (p.d_scales) {
-    qs = p.d_scales[0];
-    ks = p.d_scales[1];
-    vs = p.d_scales[2];
-  }
-  // scores in log2 units: t = c * (q . k)
-  const float c_log2 = qs * ks * p.sm_scale * 1.4426950408889634f;
+  // E8M0 operand scales of the folded form: 2^kc split over A and B
+  // (each covers 2^-127 .. 2^127)
+  const int kca = kc < -127 ? -127 : (kc > 127 ? 127 : kc);
+  const int sc_a = 127 + kca, sc_b = 127 + (kc - kca);
 
   const int64_t q_row_stride = (int64_t)p.Hq * C::KROW;
   const int64_t k_row_stride = (int64_t)p.Hkv * C::KROW;
@@ -261,50 +270,46 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   // stage no step reads any more), so every step issues the same number of
   // loads and the vmcnt bookkeeping is a constant.
   // A lane's row within its 1 KB block and its swizzled chunk depend only on
-  // the instruction, not on the tile, so each instruction's row offset and
-  // chunk byte offset are precomputed per lane; a tile adds a wave-uniform
-  // row offset. Only a tile that crosses the sequence end clamps per lane.
-  int k_lrow[C::KLOADS], k_lch[C::KLOADS], v_lrow[C::VLOADS], v_lch[C::VLOADS];
-  // byte offset of the lane's source in a tile (kept in registers for FP8;
-  // BF16, whose register budget is tighter, recomputes it per load)
-  int64_t k_loff[C::KLOADS], v_loff[C::VLOADS];
+  // the instruction, not on the tile, so each instruction's byte offset
+  // within a tile is precomputed per lane (32-bit); the tile's base address
+  // is wave-uniform and goes in a scalar register pair, so a load costs no
+  // vector instruction. Only a tile that crosses the sequence end clamps
+  // rows per lane.
+  int k_loff[C::KLOADS], v_loff[C::VLOADS];
+  const int k_stride32 = (int)k_row_stride, v_stride32 = (int)v_row_stride;
 #pragma unroll
   for (int i = 0; i < C::KLOADS; ++i) {
     const int o = (i * C::NWAVES + wave) * 1024 + 16 * lane;
-    k_lrow[i] = o / C::KROW;
-    k_lch[i] = 16 * k_swz<C::KCH>((o % C::KROW) / 16, k_lrow[i]);
-    k_loff[i] = C::FP8 ? (int64_t)k_lrow[i] * k_row_stride + k_lch[i] : 0;
+    const int row = o / C::KROW;
+    k_loff[i] = row * k_stride32 + 16 * k_swz<C::KCH>((o % C::KROW) / 16, row);
   }
 #pragma unroll
   for (int i = 0; i < C::VLOADS; ++i) {
     const int o = (i * C::NWAVES + wave) * 1024 + 16 * lane;
-    v_lrow[i] = o / C::VROW;
-    v_lch[i] = 16 * v_swz<C::VCH>((o % C::VROW) / 16, v_lrow[i]);
-    v_loff[i] = C::FP8 ? (int64_t)v_lrow[i] * v_row_stride + v_lch[i] : 0;
+    const int row = o / C::VROW;
+    v_loff[i] = row * v_stride32 + 16 * v_swz<C::VCH>((o % C::VROW) / 16, row);
   }
-  auto issue_tile = [&](const uint8_t* base, int64_t stride, const int* lrow, const int* lch, const int64_t* loff,
-                        int nloads, uint32_t dst, int n) {
+  auto issue_tile = [&](const uint8_t* base, int stride, const int* loff, int nloads, int rowbytes, uint32_t dst,
+                        int n) {
     const int nn = min(n, T - 1);
     const uint8_t* tb = base + (int64_t)(nn * BN) * stride;
     if ((nn + 1) * BN <= S) {
 #pragma unroll
-      for (int i = 0; i < nloads; ++i) {
-        const int64_t off = C::FP8 ? loff[i] : (int64_t)lrow[i] * stride + lch[i];
-        global_to_lds_16_async(tb + off, dst + (i * C::NWAVES + wave) * 1024);
-      }
+      for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst + (i * C::NWAVES + wave) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < nloads; ++i) {
-        const int key = min(nn * BN + lrow[i], S - 1);
-        global_to_lds_16_async(base + (int64_t)key * stride + lch[i], dst + (i * C::NWAVES + wave) * 1024);
+        const int row = ((i * C::NWAVES + wave) * 1024 + 16 * lane) / rowbytes;
+        const int key = min(nn * BN + row, S - 1);
+        global_to_lds_16_async(tb, loff[i] + (key - nn * BN - row) * stride, dst + (i * C::NWAVES + wave) * 1024);
       }
     }
   };
   auto issue_k = [&](int n) {
-    issue_tile(kbase, k_row_stride, k_lrow, k_lch, k_loff, C::KLOADS, k_lds_addr + (n % NS) * C::KTILE, n);
+    issue_tile(kbase, k_stride32, k_loff, C::KLOADS, C::KROW, k_lds_addr + (n % NS) * C::KTILE, n);
   };
   auto issue_v = [&](int n) {
-    issue_tile(vbase, v_row_stride, v_lrow, v_lch, v_loff, C::VLOADS, v_lds_addr + (n % NS) * C::VTILE, n);
+    issue_tile(vbase, v_stride32, v_loff, C::VLOADS, C::VROW, v_lds_addr + (n % NS) * C::VTILE, n);
   };
 
   // ---- per-lane LDS read offsets within a stage (the swizzle term depends
@@ -341,11 +346,15 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   f32x16 oacc[C::NOT];
 #pragma unroll
   for (int t = 0; t < C::NOT; ++t) oacc[t] = f32x16{};
-  // Running max of t (log2 units). Starting from a huge finite negative (not
-  // -inf) keeps fma(s, c, -m) free of inf - inf; the first tile always takes
-  // the exact path because its sums overflow the threshold.
-  float m_run = -1e30f;
+  // Running max of t (log2 units). Fma form: starting from a huge finite
+  // negative (not -inf) keeps fma(s, c, -m) free of inf - inf, and the first
+  // tile always takes the exact path because its sums overflow the
+  // threshold. Folded form: the MFMA starts each score tile from cblk =
+  // -m_run (16 copies, the shape of an accumulator), m_run starts at 0 and
+  // the first tile is sent to the exact path explicitly.
+  float m_run = FOLD ? 0.f : -1e30f;
   float l_run = 0.f;  // this lane's share of the running row sum
+  f32x16 cblk = f32x16{};
 
   // Scores and P operands are double-buffered by tile parity: step n reads
   // the scores of tile n from sbuf[n&1] and writes tile n+1's into
@@ -360,7 +369,8 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   for (int i = 0; i < PREGS; ++i) pbuf[1][i] = PVec{};
 
   // ---- matrix work of one step, as a list of MFMA jobs: P.V jobs (tile n-1)
-  // then Q.K^T jobs (tile n+1).
+  // then Q.K^T jobs (tile n+1), contraction step outermost so that two
+  // consecutive MFMAs never accumulate into the same score tile.
   typedef typename std::conditional<C::FP8, i32x8, i32x4>::type Frag;
   auto frag_reads = [](int j) constexpr -> int {
     return j < C::NPV ? (C::FP8 ? 4 : 2) : (C::FP8 ? 2 : 1);
@@ -388,7 +398,7 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
         a[3] = (int)(uint16_t)x[1][2] | ((int)(uint16_t)x[1][3] << 16);
       }
     } else {
-      const int jq = j - C::NPV, t = jq / C::QK_STEPS, u = jq % C::QK_STEPS;
+      const int jq = j - C::NPV, t = jq % C::NST, u = jq / C::NST;
       const ATTN_LDS char* kr = kl + 32 * t * C::KROW;
       if constexpr (C::FP8) {
         i32x4 a0 = lds_read_b128(kr + k_off[u][0]);
@@ -415,12 +425,12 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
         oacc[tv] = mfma_bf16(__builtin_bit_cast(bf16x8, a), pv[u], oacc[tv]);
       }
     } else {
-      const int jq = j - C::NPV, t = jq / C::QK_STEPS, u = jq % C::QK_STEPS;
-      const f32x16 acc = u == 0 ? f32x16{} : sq[t];
+      const int jq = j - C::NPV, t = jq % C::NST, u = jq / C::NST;
+      const f32x16 acc = u == 0 ? (FOLD ? cblk : f32x16{}) : sq[t];
       if constexpr (C::FP8) {
         i32x8 bq = {qf[2 * u][0], qf[2 * u][1], qf[2 * u][2], qf[2 * u][3],
                     qf[2 * u + 1][0], qf[2 * u + 1][1], qf[2 * u + 1][2], qf[2 * u + 1][3]};
-        sq[t] = mfma_f8(a, bq, acc);
+        sq[t] = FOLD ? mfma_f8_scaled(a, bq, acc, sc_a, sc_b) : mfma_f8(a, bq, acc);
       } else {
         sq[t] = mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[u]), acc);
       }
@@ -435,22 +445,31 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
   // grown well past m_run (always on the first tile). Every p then stays
   // <= 256, and the result is the same softmax: m only shifts the common
   // factor that O and l share.
+  // Fma form: t = fma(s, c, -m). Folded form: the score is t already, less
+  // `m` on the exact path (m = the increase of the running max).
   constexpr int NCHUNK = C::NST * 4;              // 4 fp32 scores per lane each
-  auto probs_chunk = [&](int c, auto Pc, float m, float& lsum) {
+  auto log2_prob = [&](float s, float m, auto SHIFTc) -> float {
+    if constexpr (!FOLD) return __builtin_fmaf(s, c_log2, -m);
+    else if constexpr (decltype(SHIFTc)::value) return s - m;
+    else return s;
+  };
+  auto probs_chunk = [&](int c, auto Pc, float m, float& lsum, auto SHIFTc) {
     constexpr int P = decltype(Pc)::value;
     const f32x16* sc = sbuf[P];
     PVec* pout = pbuf[P];
     // chunk c: score tile t = c / 4, registers r .. r+3
     const int t = c >> 2, r = 4 * (c & 3);
-    const float p0 = fast_exp2(__builtin_fmaf(sc[t][r], c_log2, -m));
-    const float p1 = fast_exp2(__builtin_fmaf(sc[t][r + 1], c_log2, -m));
-    const float p2 = fast_exp2(__builtin_fmaf(sc[t][r + 2], c_log2, -m));
-    const float p3 = fast_exp2(__builtin_fmaf(sc[t][r + 3], c_log2, -m));
+    const float p0 = fast_exp2(log2_prob(sc[t][r], m, SHIFTc));
+    const float p1 = fast_exp2(log2_prob(sc[t][r + 1], m, SHIFTc));
+    const float p2 = fast_exp2(log2_prob(sc[t][r + 2], m, SHIFTc));
+    const float p3 = fast_exp2(log2_prob(sc[t][r + 3], m, SHIFTc));
     lsum += (p0 + p1) + (p2 + p3);
     if constexpr (C::FP8) {
       // FP8 operand byte j <- score tile j/16, register j%16: chunk c fills
       // dword (c & 3) of pout[t]
-      const int x = cvt_fp8x2(p0, p1, 0, false);
+      // (both halves are written: the register's old contents only save an
+      // instruction that would clear it)
+      const int x = cvt_fp8x2(p0, p1, pout[t][c & 3], false);
       pout[t][c & 3] = pin(cvt_fp8x2(p2, p3, x, true));
     } else {
       // BF16 operand u = 2t + (r / 8) holds registers 8(u%2) .. +7 of tile t
@@ -462,10 +481,14 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
     }
   };
 
-  // exact-maximum path for a tile whose partial sums overflowed: new row
-  // max, rescale of l and O (O holds every P.V issued so far), P again.
-  auto exact_path = [&](auto Pc, float& lsum) {
-    constexpr int P = decltype(Pc)::value;
+  // exact-maximum path for a tile whose partial sums overflowed (or, folded
+  // form, the first tile): new row max, rescale of l and O (O holds every
+  // P.V issued so far), P again. Q is the parity of the next tile's scores,
+  // which the folded form computed against the old max.
+  using False_ = std::integral_constant<bool, false>;
+  using True_ = std::integral_constant<bool, true>;
+  auto exact_path = [&](auto Pc, float& lsum, bool first) {
+    constexpr int P = decltype(Pc)::value, Q = 1 - P;
     const f32x16* sc = sbuf[P];
     float mx = -INFINITY;
 #pragma unroll
@@ -473,15 +496,33 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[t][r], sc[t][r + 1]));
     mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_run, mx * c_log2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
     lsum = 0.f;
+    if constexpr (!FOLD) {
+      const float m_new = fmaxf(m_run, mx * c_log2);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int c = 0; c < NCHUNK; ++c) probs_chunk(c, Pc, m_run, lsum);
+      for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
+#pragma unroll
+      for (int c = 0; c < NCHUNK; ++c) probs_chunk(c, Pc, m_run, lsum, False_{});
+    } else {
+      // scores are t = c*s - m_run: the max grows by d = max(mx, 0) (on the
+      // first tile, where nothing is accumulated yet, it is set to mx; a row
+      // always sees key 0 there, so mx is finite)
+      const float d = first ? mx : fmaxf(mx, 0.f);
+      const float alpha = first ? 0.f : fast_exp2(-d);
+      m_run += d;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cblk[i] = -m_run;
+#pragma unroll
+      for (int t = 0; t < C::NST; ++t) sbuf[Q][t] -= d;
+#pragma unroll
+      for (int c = 0; c < NCHUNK; ++c) probs_chunk(c, Pc, d, lsum, True_{});
+    }
   };
 
   constexpr int NJOB = C::NPV + C::NQK;
@@ -528,17 +569,23 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
       // chain is complete (for the lazy-max check below) by the time the
       // last MFMAs have issued
       const int c_end = j + 2 >= NJOB ? NCHUNK : (j + 1) * NCHUNK / (NJOB - 2);
-      for (; c < c_end; ++c) probs_chunk(c, Pc, m_run, lsum);
+      for (; c < c_end; ++c) probs_chunk(c, Pc, m_run, lsum, False_{});
       // issue order: this job's look-ahead reads, then its MFMA; the softmax
       // instructions are left to the scheduler (pinning them measured slower)
-      if (j + 2 < NJOB) sched_group<kSchedDsRead>(frag_reads(j + 2));
-      sched_group<kSchedMfma>(1);
+      if constexpr (FOLD) {
+        // the scaled MFMA is not matched by scheduling groups: fence each job
+        sched_fence();
+      } else {
+        if (j + 2 < NJOB) sched_group<kSchedDsRead>(frag_reads(j + 2));
+        sched_group<kSchedMfma>(1);
+      }
     }
     wait_vmcnt<C::INFLIGHT>();
     __syncthreads();
     // lazy-max check of tile n after the barrier, by when its row sums are
     // complete (the exact path touches registers only)
-    if (wave_any(!(lsum <= kLazyMaxThreshold))) exact_path(Pc, lsum);
+    const bool first = FOLD && n == 0;
+    if (wave_any(first | !(lsum <= kLazyMaxThreshold))) exact_path(Pc, lsum, first);
     l_run += lsum;
   };
 
@@ -605,6 +652,32 @@ __global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
       p.lse[((int64_t)b * p.Hq + h) * S + qrow] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
     }
   }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NTHREADS, 2) void attn_fwd_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) char k_ring[C::NSTAGE * C::KTILE];
+  __shared__ __attribute__((aligned(1024))) char v_ring[C::NSTAGE * C::VTILE];
+  float qs = p.q_scale, ks = p.k_scale, vs = p.v_scale;
+  if (p.d_scales) {
+    qs = p.d_scales[0];
+    ks = p.d_scales[1];
+    vs = p.d_scales[2];
+  }
+  // scores in log2 units: t = c * (q . k)
+  const float c_log2 = qs * ks * p.sm_scale * 1.4426950408889634f;
+  if constexpr (C::FOLDABLE) {
+    // c = f * 2^e, f in [0.5, 1): a power of two up to fp32 rounding of the
+    // scale product (a relative 2^-18 covers it many times over)
+    int e;
+    const float f = frexpf(c_log2, &e);
+    const bool pow2 = fabsf(f - 0.5f) <= 0x1p-19f || fabsf(f - 1.0f) <= 0x1p-18f;
+    if (uniform(pow2 ? 1 : 0)) {
+      attn_fwd_body<C, kScaleFolded>(p, k_ring, v_ring, vs, c_log2, uniform(f < 0.75f ? e - 1 : e));
+      return;
+    }
+  }
+  attn_fwd_body<C, kScaleFma>(p, k_ring, v_ring, vs, c_log2, 0);
 }
 
 }  // namespace attn

@@ -26,6 +26,13 @@ __device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// The same MFMA with the product scaled by 2^(sa-127) * 2^(sb-127) (E8M0
+// operand scales, one value for every lane here); the accumulator input is
+// not scaled.
+__device__ __forceinline__ f32x16 mfma_f8_scaled(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // 32x32x16 BF16 MFMA, fp32 accumulate; same row/column/accumulator layout,
 // 8 contraction elements per lane per half.
 __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -75,17 +82,18 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const ATTN_LDS void*)p;
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at lds_addr + 16*l (lds_addr is wave-uniform; the instruction takes
-// it from M0). Issued as inline assembly so that the compiler does not
+// 16 bytes per lane from global memory straight into LDS: lane l reads
+// base + voff (base wave-uniform, in scalar registers; voff per lane) and its
+// bytes land at lds_addr + 16*l (lds_addr is wave-uniform; the instruction
+// takes it from M0). Issued as inline assembly so that the compiler does not
 // treat later LDS reads of other ring stages as dependent on it: the caller
 // tracks completion itself with wait_vmcnt() before the barrier that
 // publishes the stage. M0 is set immediately before the load, with one
 // wait state, and this file uses no other construct that needs M0.
-__device__ __forceinline__ void global_to_lds_16_async(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+__device__ __forceinline__ void global_to_lds_16_async(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(gptr), "s"(lds_addr)
+               : "v"(voff), "s"(base), "s"(lds_addr)
                : "memory", "m0");
 }
 

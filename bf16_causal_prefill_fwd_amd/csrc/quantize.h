@@ -6,8 +6,10 @@
 
 namespace attn {
 
+// d_k_scale == nullptr: plain per-tensor scale; else the folded query scale
+// for that key scale and softmax scale.
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
-                               hipStream_t stream);
+                               const float* d_k_scale, float sm_scale, hipStream_t stream);
 hipError_t launch_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream);
 
 }  // namespace attn

@@ -4,7 +4,9 @@
 // The pages fix the FP8 format (e4m3: ai4bro.com "TL;DR"; Le Fil IA, context
 // paragraph) but not the scale granularity; this library uses one fp32 scale
 // per tensor: scale = absmax / 448 (448 = largest e4m3fn value), code =
-// e4m3fn(x / scale) rounded to nearest even.
+// e4m3fn(x / scale) rounded to nearest even. A query tensor may instead take
+// the folded scale (folded_scale_from_amax), at most twice absmax / 448,
+// which turns the attention kernel's score factor into a power of two.
 //
 // Two HBM passes: a grid-wide absmax (each workgroup folds its maximum in
 // with one integer atomic max on the IEEE bits, which orders non-negative
@@ -68,11 +70,34 @@ __device__ __forceinline__ float scale_from_amax(uint32_t bits) {
   return a == 0.f ? 1.f : __fdiv_rn(a, 448.f);
 }
 
+// Folded scale of a query tensor: the smallest scale of the form
+// 2^j / (k_scale * softmax_scale * log2 e) that is >= absmax / 448, so that
+// the attention kernel's score factor q_scale * k_scale * softmax_scale *
+// log2 e is the power of two 2^j (up to the fp32 rounding of the stored
+// scale) and goes into the MFMA's operand scales. Computed in fp64 (each
+// step correctly rounded), rounded once to fp32; 1.0 for an all-zero tensor.
+__device__ __forceinline__ float folded_scale_from_amax(uint32_t bits, float k_scale, float sm_scale) {
+  const float a = __uint_as_float(bits);
+  if (a == 0.f) return 1.f;
+  const double g = (double)k_scale * (double)sm_scale * 1.4426950408889634;
+  const double t = ((double)a / 448.0) * g;
+  int e;
+  const double f = frexp(t, &e);  // t = f * 2^e, f in [0.5, 1)
+  const int j = f == 0.5 ? e - 1 : e;
+  return (float)(ldexp(1.0, j) / g);
+}
+
+// The scale the cast uses: plain (d_k_scale == nullptr) or folded.
+__device__ __forceinline__ float quant_scale(uint32_t bits, const float* d_k_scale, float sm_scale) {
+  return d_k_scale ? folded_scale_from_amax(bits, *d_k_scale, sm_scale) : scale_from_amax(bits);
+}
+
 template <int XDT>
 __global__ __launch_bounds__(QTHREADS) void quant_kernel(const void* __restrict__ x, int64_t n,
                                                           const uint32_t* __restrict__ amax_bits,
+                                                          const float* __restrict__ d_k_scale, float sm_scale,
                                                           uint8_t* __restrict__ out) {
-  const float scale = scale_from_amax(*amax_bits);
+  const float scale = quant_scale(*amax_bits, d_k_scale, sm_scale);
   const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
   const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
   const int64_t n8 = n / 8;
@@ -106,8 +131,8 @@ __global__ __launch_bounds__(QTHREADS) void quant_kernel(const void* __restrict_
   }
 }
 
-__global__ void scale_finalize_kernel(uint32_t* amax_bits) {
-  *amax_bits = __float_as_uint(scale_from_amax(*amax_bits));
+__global__ void scale_finalize_kernel(uint32_t* amax_bits, const float* d_k_scale, float sm_scale) {
+  *amax_bits = __float_as_uint(quant_scale(*amax_bits, d_k_scale, sm_scale));
 }
 
 // fp32 -> bf16, round to nearest even (finite inputs).
@@ -145,18 +170,18 @@ static int stream_grid(int64_t n) {
 }
 
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
-                               hipStream_t stream) {
+                               const float* d_k_scale, float sm_scale, hipStream_t stream) {
   uint32_t* bits = (uint32_t*)d_scale;
   const int grid = stream_grid(n);
   hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, bits);
   if (x_dtype == 0) {
     hipLaunchKernelGGL(amax_kernel<0>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits);
-    hipLaunchKernelGGL(quant_kernel<0>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits, x8);
+    hipLaunchKernelGGL(quant_kernel<0>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits, d_k_scale, sm_scale, x8);
   } else {
     hipLaunchKernelGGL(amax_kernel<1>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits);
-    hipLaunchKernelGGL(quant_kernel<1>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits, x8);
+    hipLaunchKernelGGL(quant_kernel<1>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits, d_k_scale, sm_scale, x8);
   }
-  hipLaunchKernelGGL(scale_finalize_kernel, dim3(1), dim3(1), 0, stream, bits);
+  hipLaunchKernelGGL(scale_finalize_kernel, dim3(1), dim3(1), 0, stream, bits, d_k_scale, sm_scale);
   return hipGetLastError();
 }
 

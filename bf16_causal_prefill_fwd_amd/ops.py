@@ -38,6 +38,8 @@ _SIGNATURES = {
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      _c_void_p]),
     "attn_quantize_fp8": (_c_int, [_c_void_p, _c_int, _c_int64, _c_void_p, _c_void_p, _c_void_p]),
+    "attn_quantize_fp8_q": (_c_int, [_c_void_p, _c_int, _c_int64, _c_void_p, _c_void_p, _c_void_p, _c_float,
+                                     _c_void_p]),
     "attn_cast_bf16": (_c_int, [_c_void_p, _c_int64, _c_void_p, _c_void_p]),
     "attn_strerror": (ctypes.c_char_p, [_c_int]),
     "attn_abi_version": (_c_int, []),
@@ -98,9 +100,12 @@ def _need(t: torch.Tensor, name: str):
 
 
 def attn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None, scale: torch.Tensor | None = None,
-                      stream=None):
+                      stream=None, k_scale: torch.Tensor | None = None, softmax_scale: float | None = None):
     """Per-tensor e4m3fn quantization on the device.
 
+    With ``k_scale`` (the key tensor's device scale) and ``softmax_scale``
+    this is the query form (attn_quantize_fp8_q): the scale is folded so that
+    q_scale * k_scale * softmax_scale * log2(e) is a power of two.
     Returns (codes uint8 tensor shaped like x, scale float32 device tensor [1]).
     """
     _need(x, "x")
@@ -113,8 +118,17 @@ def attn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None, scale: t
     out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
     scale = torch.empty(1, dtype=torch.float32, device=x.device) if scale is None else scale
     _need(out, "out")
-    _check("attn_quantize_fp8",
-           lib().attn_quantize_fp8(x.data_ptr(), xdt, x.numel(), out.data_ptr(), scale.data_ptr(), _stream(stream)))
+    if k_scale is None:
+        _check("attn_quantize_fp8",
+               lib().attn_quantize_fp8(x.data_ptr(), xdt, x.numel(), out.data_ptr(), scale.data_ptr(),
+                                       _stream(stream)))
+    else:
+        _need(k_scale, "k_scale")
+        if softmax_scale is None:
+            raise ValueError("the folded query scale needs softmax_scale")
+        _check("attn_quantize_fp8_q",
+               lib().attn_quantize_fp8_q(x.data_ptr(), xdt, x.numel(), out.data_ptr(), scale.data_ptr(),
+                                         k_scale.data_ptr(), float(softmax_scale), _stream(stream)))
     return out, scale
 
 
@@ -179,18 +193,23 @@ def attn_prefill_fwd(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True
 
 
 def prefill(q32: torch.Tensor, k32: torch.Tensor, v32: torch.Tensor, dtype: str = "fp8", causal=True,
-            stream=None):
+            stream=None, fold_q: bool = True):
     """The whole path on float32 device inputs: input step, then attention.
 
     dtype "fp8": per-tensor quantization (scales stay on the device and are
-    read by the kernel, so no host synchronisation); "bf16": RNE cast.
+    read by the kernel, so no host synchronisation); with ``fold_q`` the query
+    takes the folded scale (see attn_quantize_fp8). "bf16": RNE cast.
     Returns (o, lse, extras) where extras holds the codes and the scale tensor.
     """
     if dtype == "fp8":
         scales = torch.empty(3, dtype=torch.float32, device=q32.device)
-        q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream)
         k8, _ = attn_quantize_fp8(k32, scale=scales[1:2], stream=stream)
         v8, _ = attn_quantize_fp8(v32, scale=scales[2:3], stream=stream)
+        if fold_q:
+            q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream, k_scale=scales[1:2],
+                                      softmax_scale=1.0 / math.sqrt(q32.shape[-1]))
+        else:
+            q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream)
         o, lse = attn_prefill_fwd(q8, k8, v8, causal=causal, d_scales=scales, stream=stream)
         return o, lse, dict(q=q8, k=k8, v=v8, scales=scales)
     if dtype == "bf16":

@@ -71,7 +71,8 @@ enum {
  *   d_qk, d_v   head dims; supported: (128, 128) and (192, 128).
  *   causal      1: key j visible to query i iff j <= i; 0: all keys visible.
  *   dtype       ATTN_DTYPE_FP8_E4M3 or ATTN_DTYPE_BF16.
- * Limits: B*S*Hq*max(d_qk,d_v) < 2^40 elements; S <= 2^24.
+ * Limits: B*S*Hq*max(d_qk,d_v) < 2^40 elements; S <= 2^24;
+ *         Hkv*max(d_qk,d_v) < 2^24.
  */
 int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      float q_scale, float k_scale, float v_scale,
@@ -105,6 +106,26 @@ int attn_prefill_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
  */
 int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
                       hipStream_t stream);
+
+/*
+ * The same step for a QUERY tensor, with the scale folded for the kernel:
+ *   d_k_scale      device pointer to the key tensor's scale (one float,
+ *                  e.g. the d_scale of attn_quantize_fp8 on k), read on
+ *                  the device after the work queued before this call.
+ *   softmax_scale  the softmax scale the attention call will use (> 0,
+ *                  finite; 1/sqrt(d_qk) for attn_prefill_fwd).
+ * d_scale receives the smallest scale 2^j / (k_scale * softmax_scale *
+ * log2(e)), j an integer, that is >= absmax(|x|)/448 (so at most twice it),
+ * evaluated in fp64 with correctly rounded steps and rounded once to fp32;
+ * 1.0 when x is all zeros. Codes are e4m3fn(x / scale) as above. The product
+ * q_scale * k_scale * softmax_scale * log2(e) is then a power of two, which
+ * lets the attention kernel apply it through the FP8 MFMA's power-of-two
+ * operand scales instead of one vector multiply per score (the kernel
+ * detects this by itself; any other scale takes the general path). d_k_scale
+ * must not overlap d_scale.
+ */
+int attn_quantize_fp8_q(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
+                        const float* d_k_scale, float softmax_scale, hipStream_t stream);
 
 /*
  * BF16 input step: float32 -> bfloat16, round to nearest, ties to even.

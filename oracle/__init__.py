@@ -22,7 +22,8 @@ section):
 Modules:
 
 * ``formats``   -- OCP e4m3fn and bfloat16 encoders/decoders written from the
-  format definitions, and the per-tensor absmax quantizer.
+  format definitions, the per-tensor absmax quantizer and its folded query
+  scale.
 * ``attention`` -- exact causal softmax attention in float64 on dequantized
   inputs: O and the natural-log log-sum-exp, for whole tensors or for
   selected rows.
@@ -40,6 +41,7 @@ from .formats import (
     bf16_encode,
     quantize_fp8_per_tensor,
     per_tensor_scale,
+    per_tensor_scale_folded,
     encode_with_scale,
     dequantize_fp8,
 )
@@ -57,6 +59,7 @@ __all__ = [
     "bf16_encode",
     "quantize_fp8_per_tensor",
     "per_tensor_scale",
+    "per_tensor_scale_folded",
     "encode_with_scale",
     "dequantize_fp8",
     "causal_attention",

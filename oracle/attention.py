@@ -35,7 +35,8 @@ import math
 
 import numpy as np
 
-from .formats import bf16_decode, bf16_encode, dequantize_fp8, encode_with_scale, per_tensor_scale
+from .formats import (bf16_decode, bf16_encode, dequantize_fp8, encode_with_scale, per_tensor_scale,
+                      per_tensor_scale_folded)
 
 
 def _check_shapes(q, k, v):
@@ -144,11 +145,14 @@ class _QuantizedView:
     encoded, so rows of very long sequences stay cheap.
     """
 
-    def __init__(self, x32, kind):
+    def __init__(self, x32, kind, scale=None):
         self.x32 = np.asarray(x32, dtype=np.float32)
         self.kind = kind
         self.shape = self.x32.shape
-        self.scale = per_tensor_scale(self.x32) if kind == "fp8" else np.float32(1.0)
+        if kind != "fp8":
+            self.scale = np.float32(1.0)
+        else:
+            self.scale = per_tensor_scale(self.x32) if scale is None else np.float32(scale)
 
     def codes(self, idx=slice(None)):
         if self.kind == "fp8":
@@ -163,10 +167,12 @@ class _QuantizedView:
 
 
 def prefill_reference(q32, k32, v32, dtype: str, causal: bool = True, rows=None,
-                      softmax_scale: float | None = None):
+                      softmax_scale: float | None = None, fold_q: bool = False):
     """The whole path on float32 inputs: the input step, then attention.
 
-    dtype "fp8": per-tensor absmax e4m3fn codes and scales; "bf16": bf16 RNE.
+    dtype "fp8": per-tensor absmax e4m3fn codes and scales (with ``fold_q``
+    the query takes the folded scale for the key scale and softmax scale);
+    "bf16": bf16 RNE.
     Attention runs in float64 on the dequantized values. Without ``rows``:
     returns the codes (uint8 for fp8, uint16 bit patterns for bf16), the
     scales (1.0 for bf16) and the full O / LSE. With ``rows`` (a list of
@@ -175,7 +181,12 @@ def prefill_reference(q32, k32, v32, dtype: str, causal: bool = True, rows=None,
     """
     if dtype not in ("fp8", "bf16"):
         raise ValueError("dtype must be 'fp8' or 'bf16'")
-    views = [_QuantizedView(t, dtype) for t in (q32, k32, v32)]
+    kv = [_QuantizedView(t, dtype) for t in (k32, v32)]
+    q_scale = None
+    if dtype == "fp8" and fold_q:
+        sm = 1.0 / math.sqrt(np.shape(q32)[-1]) if softmax_scale is None else softmax_scale
+        q_scale = per_tensor_scale_folded(q32, kv[0].scale, sm)
+    views = [_QuantizedView(q32, dtype, q_scale)] + kv
     out = dict(q_scale=views[0].scale, k_scale=views[1].scale, v_scale=views[2].scale, views=views)
     if rows is None:
         qc, kc, vc = (vw.codes() for vw in views)

@@ -22,6 +22,16 @@ value nearest to x / scale (the division in fp32, correctly rounded), ties to
 the even code. A tensor of zeros gets scale 1. The dequantized value is
 decode(code) * scale, exact in float64.
 
+Folded query scale (a reading of the quantize step, also not on the pages):
+a query tensor may take, instead of absmax / 448, the smallest scale of the
+form 2^j / (k_scale * softmax_scale * log2 e), j an integer, that is at least
+absmax / 448. It is evaluated in float64 with each operation correctly
+rounded -- g = (k_scale * softmax_scale) * log2e, t = (absmax / 448) * g,
+j = ceil(log2 t) exactly, scale = 2^j / g -- and rounded once to fp32; a
+tensor of zeros gets scale 1. It is then at most twice absmax / 448, codes
+are formed as above, and q_scale * k_scale * softmax_scale * log2 e is a
+power of two.
+
 bfloat16 is the top 16 bits of an IEEE binary32: 1 sign, 8 exponent, 7
 mantissa bits. Encoding from fp32 rounds to the nearest bfloat16, ties to the
 even mantissa.
@@ -29,9 +39,13 @@ even mantissa.
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 E4M3_MAX = 448.0
+# log2(e) rounded to float64
+LOG2E = 1.4426950408889634
 
 
 def e4m3fn_decode(codes: np.ndarray) -> np.ndarray:
@@ -102,6 +116,19 @@ def per_tensor_scale(x: np.ndarray) -> np.float32:
     if amax == 0:
         return np.float32(1.0)
     return np.float32(amax / np.float32(E4M3_MAX))
+
+
+def per_tensor_scale_folded(x: np.ndarray, k_scale, softmax_scale) -> np.float32:
+    """The folded query scale: smallest 2^j / (k_scale*softmax_scale*log2 e) >= absmax/448."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    if amax == 0.0:
+        return np.float32(1.0)
+    g = float(np.float64(np.float32(k_scale)) * np.float64(np.float32(softmax_scale))) * LOG2E
+    t = (amax / E4M3_MAX) * g
+    f, e = math.frexp(t)  # t = f * 2^e, 0.5 <= f < 1
+    j = e - 1 if f == 0.5 else e
+    return np.float32(math.ldexp(1.0, j) / g)
 
 
 def encode_with_scale(x: np.ndarray, scale) -> np.ndarray:

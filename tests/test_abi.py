@@ -22,8 +22,8 @@ FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced by host
 
 def test_exports_every_header_function():
     names = ops.header_functions()
-    assert set(names) == {"attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_quantize_fp8", "attn_cast_bf16",
-                          "attn_strerror", "attn_abi_version"}
+    assert set(names) == {"attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_quantize_fp8", "attn_quantize_fp8_q",
+                          "attn_cast_bf16", "attn_strerror", "attn_abi_version"}
     L = ctypes.CDLL(build_mod.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -58,6 +58,7 @@ def _fwd(**kw):
     (dict(vs=float("nan")), INVALID),
     (dict(q=FAKE + 4), INVALID),
     (dict(S=(1 << 24) + 1), INVALID),
+    (dict(Hq=1 << 17, Hkv=1 << 17), INVALID),  # a 64-row K tile would span >= 2^31 bytes
     (dict(dtype=7), UNSUPPORTED),
     (dict(dqk=64, dv=64), UNSUPPORTED),
     (dict(dqk=192, dv=192), UNSUPPORTED),
@@ -72,6 +73,17 @@ def test_fwd_ex_rejects_bad_softmax_scale_and_scale_pointer():
     args = [FAKE, FAKE, FAKE, FAKE, None, 1.0, 1.0, 1.0, None]
     assert f(*args, 0.0, 1, 64, 2, 2, 128, 128, 1, 0, None) == INVALID
     assert f(*args[:8], FAKE + 2, 0.1, 1, 64, 2, 2, 128, 128, 1, 0, None) == INVALID
+
+
+def test_quantize_q_rejects_bad_arguments():
+    L = ops.lib()
+    f = L.attn_quantize_fp8_q
+    assert f(FAKE, 0, 16, FAKE, FAKE + 64, None, 0.1, None) == INVALID        # no key scale
+    assert f(FAKE, 0, 16, FAKE, FAKE + 64, FAKE + 128, 0.0, None) == INVALID  # softmax scale 0
+    assert f(FAKE, 0, 16, FAKE, FAKE + 64, FAKE + 128, float("inf"), None) == INVALID
+    assert f(FAKE, 0, 16, FAKE, FAKE + 64, FAKE + 66, 0.1, None) == INVALID   # misaligned key scale
+    assert f(FAKE, 0, 16, FAKE, FAKE + 64, FAKE + 64, 0.1, None) == INVALID   # key scale aliases d_scale
+    assert f(FAKE, 3, 16, FAKE, FAKE + 64, FAKE + 128, 0.1, None) == UNSUPPORTED
 
 
 def test_quantize_and_cast_reject_bad_arguments():

@@ -41,11 +41,11 @@ def codes_np(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def run_case(w: Workload, seed: int):
+def run_case(w: Workload, seed: int, fold_q: bool = True):
     q, k, v = make_inputs(w, seed)
     print(f"case {w.name} B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d_qk}/{w.d_v} {w.dtype} "
-          f"causal={w.causal} seed={seed}", flush=True)
-    o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), w.dtype, causal=w.causal)
+          f"causal={w.causal} seed={seed} fold_q={fold_q}", flush=True)
+    o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), w.dtype, causal=w.causal, fold_q=fold_q)
     torch.cuda.synchronize()
     return q, k, v, o, lse, ex
 
@@ -65,10 +65,16 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
-def test_small_full_oracle(w):
-    q, k, v, o, lse, ex = run_case(w, seed=1)
-    ref = prefill_reference(q, k, v, w.dtype, causal=w.causal)
+# FP8 cases run twice: with the folded query scale (the kernel's folded score
+# form) and with the plain per-tensor scale (its fma form)
+SMALL_RUNS = [(w, True) for w in SMALL] + [(w, False) for w in SMALL if w.dtype == "fp8"]
+
+
+@pytest.mark.parametrize("w,fold_q", SMALL_RUNS,
+                         ids=[w.name + ("" if f else "_plain_q") for w, f in SMALL_RUNS])
+def test_small_full_oracle(w, fold_q):
+    q, k, v, o, lse, ex = run_case(w, seed=1, fold_q=fold_q)
+    ref = prefill_reference(q, k, v, w.dtype, causal=w.causal, fold_q=fold_q)
     for name in ("q", "k", "v"):
         assert np.array_equal(codes_np(ex[name]), ref[name + "_codes"]), f"{name} codes differ"
     if w.dtype == "fp8":
@@ -82,6 +88,9 @@ def test_small_full_oracle(w):
     print(f"  O rel-L2 {err:.3e}  LSE max-abs {lerr:.3e}", flush=True)
     assert err <= O_TOL[w.dtype]
     assert lerr <= LSE_TOL
+    # a second launch is bit-identical
+    o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], causal=w.causal, d_scales=ex["scales"])
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(l2, lse)
 
 
 @pytest.mark.parametrize("dtype", ["fp8", "bf16"])
@@ -162,7 +171,7 @@ def test_full_size_sampled_rows(name):
     q, k, v, o, lse, ex = run_case(w, seed=0)
     rng = np.random.default_rng(12345)
     rows = sample_rows(w, rng)
-    ref = prefill_reference(q, k, v, w.dtype, rows=rows)
+    ref = prefill_reference(q, k, v, w.dtype, rows=rows, fold_q=True)
     if w.dtype == "fp8":
         sc = ex["scales"].cpu().numpy()
         assert np.array_equal(sc, np.float32([ref["q_scale"], ref["k_scale"], ref["v_scale"]]))

@@ -25,8 +25,11 @@ from oracle import (
     causal_attention,
     e4m3fn_decode,
     e4m3fn_encode,
+    per_tensor_scale,
+    per_tensor_scale_folded,
     prefill_reference,
     quantize_fp8_per_tensor,
+    encode_with_scale,
 )
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -96,6 +99,54 @@ def test_quantizer_matches_torch_cast():
 def test_quantizer_zero_tensor():
     codes, scale = quantize_fp8_per_tensor(np.zeros((3, 5), np.float32))
     assert scale == 1.0 and not codes.any()
+
+
+def _folded_cases():
+    rng = np.random.default_rng(41)
+    for i in range(300):
+        x = (rng.standard_normal(257) * 10.0 ** rng.uniform(-6, 6)).astype(np.float32)
+        ks = np.float32(10.0 ** rng.uniform(-8, 2))
+        sm = np.float32(1.0 / math.sqrt([64, 128, 192, 256][i % 4]))
+        yield x, ks, sm
+
+
+def test_folded_scale_by_search_and_bounds():
+    # j found by a plain search over integers (not frexp), the bounds of the
+    # definition, and the power-of-two product, checked in exact rationals
+    from fractions import Fraction
+    for x, ks, sm in _folded_cases():
+        a = float(np.max(np.abs(x)))
+        g = (float(ks) * float(sm)) * math.log2(math.e)
+        t = (a / 448.0) * g
+        j = next(jj for jj in range(-300, 300) if 2.0 ** jj >= t)
+        assert 2.0 ** (j - 1) < t
+        sc = per_tensor_scale_folded(x, ks, sm)
+        assert sc == np.float32(2.0 ** j / g)
+        base = Fraction(a) / 448
+        assert Fraction(float(sc)) >= base * (1 - Fraction(1, 2 ** 23))
+        assert Fraction(float(sc)) < 2 * base * (1 + Fraction(1, 2 ** 22))
+        prod = Fraction(float(sc)) * Fraction(float(ks)) * Fraction(float(sm)) * Fraction(math.log2(math.e))
+        assert abs(prod / Fraction(2) ** j - 1) < Fraction(1, 2 ** 22)
+        # codes stay in range: nothing overflows to NaN and |value| <= 448
+        dec = e4m3fn_decode(encode_with_scale(x, sc))
+        assert np.all(np.isfinite(dec)) and np.abs(dec).max() <= 448.0
+        # never below the plain scale's precision: at most one binade coarser
+        assert sc >= per_tensor_scale(x) * np.float32(1 - 2 ** -22)
+
+
+def test_folded_scale_zero_tensor_and_exact_power():
+    assert per_tensor_scale_folded(np.zeros(9, np.float32), np.float32(0.5), np.float32(0.125)) == 1.0
+    # absmax/448 * g exactly a power of two: the plain scale is already folded.
+    # k_scale * sm * log2(e) is rounded in fp64, so pick absmax so that
+    # (absmax/448) * g is 2^-3 up to that rounding and check the result lands
+    # on 2^-3 / g itself.
+    ks, sm = np.float32(2.0 ** -4), np.float32(2.0 ** -3)
+    g = (float(ks) * float(sm)) * math.log2(math.e)
+    a = np.float32(448.0 * 2.0 ** -3 / g)
+    x = np.array([a, -a / 2, 1.0], np.float32)
+    sc = per_tensor_scale_folded(x, ks, sm)
+    j = math.ceil(math.log2((float(a) / 448.0) * g))
+    assert sc == np.float32(2.0 ** j / g) and j in (-3, -2)
 
 
 def test_bf16_encode_matches_torch():

@@ -86,3 +86,33 @@ def _identity():
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_mutant(name):
     assert not _pins_pass(_mutant(name)), f"mutant {name} survived the pins"
+
+
+# ----------------------------------------------------------------- folded query scale
+
+import oracle.formats as fmt_mod
+from tests.test_oracle import test_folded_scale_by_search_and_bounds
+
+FOLD_MUTANTS = {
+    "rounds_down": ("j = e - 1 if f == 0.5 else e", "j = e - 1"),
+    "drops_log2e": ("np.float64(np.float32(softmax_scale))) * LOG2E",
+                    "np.float64(np.float32(softmax_scale)))"),
+    "natural_log_base": ("np.float64(np.float32(softmax_scale))) * LOG2E",
+                         "np.float64(np.float32(softmax_scale))) / LOG2E"),
+    "half_range": ("t = (amax / E4M3_MAX) * g", "t = (amax / (E4M3_MAX / 2)) * g"),
+    "plain_scale_kept": ("return np.float32(math.ldexp(1.0, j) / g)", "return np.float32(amax / E4M3_MAX)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FOLD_MUTANTS))
+def test_pins_catch_folded_scale_mutant(name, monkeypatch):
+    old, new = FOLD_MUTANTS[name]
+    src = inspect.getsource(fmt_mod)
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("oracle._fold_mutant_" + name)
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), "<mutant %s>" % name, "exec"), mod.__dict__)
+    import tests.test_oracle as pins
+    monkeypatch.setattr(pins, "per_tensor_scale_folded", mod.per_tensor_scale_folded)
+    with pytest.raises(AssertionError):
+        test_folded_scale_by_search_and_bounds()
