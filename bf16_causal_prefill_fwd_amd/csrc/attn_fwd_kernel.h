@@ -73,6 +73,7 @@ struct FwdCfg {
   static constexpr int KTILE = BN * KROW;
   static constexpr int VTILE = BN * VROW;
   static constexpr int NSTAGE = NSTAGE_;             // K ring and V ring depth
+  static constexpr int LOOKAHEAD = 2;                // MFMA jobs whose LDS operand reads are in flight
   // folded score form available (the scaled MFMA exists for FP8 only)
   static constexpr bool FOLDABLE = FP8;
   static constexpr int LDS_BYTES = NSTAGE * (KTILE + VTILE);
@@ -548,17 +549,22 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     const ATTN_LDS char* vl = v_lds + (n == 0 ? 0 : (n - 1) % NS) * C::VTILE;
     const ATTN_LDS char* kl = k_lds + ((n + 1) % NS) * C::KTILE;
     // MFMA jobs interleaved with the softmax chunks of tile n; job j's LDS
-    // reads go out two jobs ahead (3-deep operand ring)
+    // reads go out LOOKAHEAD jobs ahead (a ring of LOOKAHEAD + 1 operands)
     float lsum = 0.f;
-    Frag fr[3];
-    fr[0] = load_frag(0, vl, kl);
-    fr[1] = load_frag(1, vl, kl);
-    sched_group<kSchedDsRead>(frag_reads(0) + frag_reads(1));
+    constexpr int LA = C::LOOKAHEAD;
+    Frag fr[LA + 1];
+    int reads0 = 0;
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+      fr[j] = load_frag(j, vl, kl);
+      reads0 += frag_reads(j);
+    }
+    sched_group<kSchedDsRead>(reads0);
     int c = 0;
 #pragma unroll
     for (int j = 0; j < NJOB; ++j) {
-      if (j + 2 < NJOB) fr[(j + 2) % 3] = load_frag(j + 2, vl, kl);
-      run_job(j, fr[j % 3], std::integral_constant<int, Q>{}, std::integral_constant<int, Q>{});
+      if (j + LA < NJOB) fr[(j + LA) % (LA + 1)] = load_frag(j + LA, vl, kl);
+      run_job(j, fr[j % (LA + 1)], std::integral_constant<int, Q>{}, std::integral_constant<int, Q>{});
       // this step's loads (K(n+NS), V(n+NS-2)) go out behind the first MFMA,
       // so their address arithmetic overlaps the softmax
       if (j == 0) {
@@ -576,7 +582,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
         // the scaled MFMA is not matched by scheduling groups: fence each job
         sched_fence();
       } else {
-        if (j + 2 < NJOB) sched_group<kSchedDsRead>(frag_reads(j + 2));
+        if (j + LA < NJOB) sched_group<kSchedDsRead>(frag_reads(j + LA));
         sched_group<kSchedMfma>(1);
       }
     }

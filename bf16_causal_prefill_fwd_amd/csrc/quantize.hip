@@ -23,34 +23,62 @@ __global__ void amax_reset_kernel(uint32_t* amax_bits) { *amax_bits = 0u; }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t u16) { return __uint_as_float(u16 << 16); }
 
-// x: 8 elements per thread-iteration (fp32: two 16-byte loads; bf16: one).
+// Inputs are streamed as 16-byte vectors (4 fp32 or 8 bf16 elements); each
+// thread loads kVecsInFlight consecutive vectors per trip (all issued before
+// any is used), so a wave's trip covers one contiguous span of
+// 64 * kVecsInFlight * 16 bytes.
+constexpr int kVecsInFlight = 4;
+
 template <int XDT>
-__global__ __launch_bounds__(QTHREADS) void amax_kernel(const void* __restrict__ x, int64_t n,
-                                                         uint32_t* amax_bits) {
-  float m = 0.f;
-  const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
-  const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
-  const int64_t n8 = n / 8;
-  for (int64_t i = gtid; i < n8; i += nthreads) {
+struct In16 {
+  static constexpr int N = XDT == 0 ? 4 : 8;  // elements per 16-byte vector
+  __device__ static void unpack(const uint4& w, float* v) {
     if constexpr (XDT == 0) {
-      const float4* p = (const float4*)x + 2 * i;
-      float4 a = p[0], c = p[1];
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+      v[0] = __uint_as_float(w.x); v[1] = __uint_as_float(w.y);
+      v[2] = __uint_as_float(w.z); v[3] = __uint_as_float(w.w);
     } else {
-      uint4 a = ((const uint4*)x)[i];
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        m = fmaxf(m, fabsf(bf16_bits_to_float(w[j] & 0xFFFFu)));
-        m = fmaxf(m, fabsf(bf16_bits_to_float(w[j] >> 16)));
+        v[2 * j] = bf16_bits_to_float(u[j] & 0xFFFFu);
+        v[2 * j + 1] = bf16_bits_to_float(u[j] >> 16);
       }
     }
   }
-  for (int64_t i = n8 * 8 + gtid; i < n; i += nthreads) {
-    float v = XDT == 0 ? ((const float*)x)[i] : bf16_bits_to_float(((const uint16_t*)x)[i]);
-    m = fmaxf(m, fabsf(v));
+  __device__ static float load1(const void* x, int64_t i) {
+    return XDT == 0 ? ((const float*)x)[i] : bf16_bits_to_float(((const uint16_t*)x)[i]);
   }
+};
+
+template <int XDT>
+__device__ __forceinline__ float absmax16(const uint4& w) {
+  float v[In16<XDT>::N];
+  In16<XDT>::unpack(w, v);
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < In16<XDT>::N; ++j) m = fmaxf(m, fabsf(v[j]));
+  return m;
+}
+
+template <int XDT>
+__global__ __launch_bounds__(QTHREADS) void amax_kernel(const void* __restrict__ x, int64_t n,
+                                                         uint32_t* amax_bits) {
+  constexpr int N = In16<XDT>::N, U = kVecsInFlight;
+  float m = 0.f;
+  const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
+  const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
+  const int64_t nv = n / N;
+  const uint4* xv = (const uint4*)x;
+  const int64_t ntrips = nv / U;
+  for (int64_t t = gtid; t < ntrips; t += nthreads) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = xv[t * U + u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = fmaxf(m, absmax16<XDT>(w[u]));
+  }
+  for (int64_t i = ntrips * U + gtid; i < nv; i += nthreads) m = fmaxf(m, absmax16<XDT>(xv[i]));
+  for (int64_t e = nv * N + gtid; e < n; e += nthreads) m = fmaxf(m, fabsf(In16<XDT>::load1(x, e)));
   // wave reduction, then across the workgroup's 4 waves
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -98,37 +126,37 @@ __global__ __launch_bounds__(QTHREADS) void quant_kernel(const void* __restrict_
                                                           const float* __restrict__ d_k_scale, float sm_scale,
                                                           uint8_t* __restrict__ out) {
   const float scale = quant_scale(*amax_bits, d_k_scale, sm_scale);
+  constexpr int N = In16<XDT>::N, U = kVecsInFlight;
   const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
   const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
-  const int64_t n8 = n / 8;
-  for (int64_t i = gtid; i < n8; i += nthreads) {
-    float v[8];
-    if constexpr (XDT == 0) {
-      const float4* p = (const float4*)x + 2 * i;
-      float4 a = p[0], c = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
-    } else {
-      uint4 a = ((const uint4*)x)[i];
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+  const int64_t nv = n / N;
+  const uint4* xv = (const uint4*)x;
+  // N codes of one vector: 4 bytes (fp32 input) or 8 bytes (bf16 input)
+  auto encode = [&](const uint4& w, int64_t vi) {
+    float v[N];
+    In16<XDT>::unpack(w, v);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
-        v[2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
-      }
+    for (int j = 0; j < N; ++j) v[j] = __fdiv_rn(v[j], scale);
+    int c[N / 4];
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const int lo = cvt_fp8x2(v[4 * q], v[4 * q + 1], 0, false);
+      c[q] = cvt_fp8x2(v[4 * q + 2], v[4 * q + 3], lo, true);
     }
+    if constexpr (N == 4) ((uint32_t*)out)[vi] = (uint32_t)c[0];
+    else ((uint2*)out)[vi] = make_uint2((uint32_t)c[0], (uint32_t)c[1]);
+  };
+  const int64_t ntrips = nv / U;
+  for (int64_t t = gtid; t < ntrips; t += nthreads) {
+    uint4 w[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = __fdiv_rn(v[j], scale);
-    int lo = cvt_fp8x2(v[0], v[1], 0, false);
-    lo = cvt_fp8x2(v[2], v[3], lo, true);
-    int hi = cvt_fp8x2(v[4], v[5], 0, false);
-    hi = cvt_fp8x2(v[6], v[7], hi, true);
-    ((uint2*)out)[i] = make_uint2((uint32_t)lo, (uint32_t)hi);
+    for (int u = 0; u < U; ++u) w[u] = xv[t * U + u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) encode(w[u], t * U + u);
   }
-  for (int64_t i = n8 * 8 + gtid; i < n; i += nthreads) {
-    float v = XDT == 0 ? ((const float*)x)[i] : bf16_bits_to_float(((const uint16_t*)x)[i]);
-    out[i] = (uint8_t)(cvt_fp8x2(__fdiv_rn(v, scale), 0.f, 0, false) & 0xFF);
-  }
+  for (int64_t i = ntrips * U + gtid; i < nv; i += nthreads) encode(xv[i], i);
+  for (int64_t e = nv * N + gtid; e < n; e += nthreads)
+    out[e] = (uint8_t)(cvt_fp8x2(__fdiv_rn(In16<XDT>::load1(x, e), scale), 0.f, 0, false) & 0xFF);
 }
 
 __global__ void scale_finalize_kernel(uint32_t* amax_bits, const float* d_k_scale, float sm_scale) {
@@ -144,25 +172,30 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __global__ __launch_bounds__(QTHREADS) void cast_bf16_kernel(const float* __restrict__ x, int64_t n,
                                                               uint16_t* __restrict__ y) {
+  constexpr int U = kVecsInFlight;
   const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
   const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
-  const int64_t n8 = n / 8;
-  for (int64_t i = gtid; i < n8; i += nthreads) {
-    const float4* p = (const float4*)x + 2 * i;
-    float4 a = p[0], c = p[1];
-    uint4 o;
-    o.x = f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16);
-    o.y = f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16);
-    o.z = f32_to_bf16_rne(c.x) | (f32_to_bf16_rne(c.y) << 16);
-    o.w = f32_to_bf16_rne(c.z) | (f32_to_bf16_rne(c.w) << 16);
-    ((uint4*)y)[i] = o;
+  const int64_t nv = n / 4;
+  const uint4* xv = (const uint4*)x;
+  auto cast4 = [&](const uint4& w, int64_t vi) {
+    ((uint2*)y)[vi] = make_uint2(f32_to_bf16_rne(__uint_as_float(w.x)) | (f32_to_bf16_rne(__uint_as_float(w.y)) << 16),
+                                 f32_to_bf16_rne(__uint_as_float(w.z)) | (f32_to_bf16_rne(__uint_as_float(w.w)) << 16));
+  };
+  const int64_t ntrips = nv / U;
+  for (int64_t t = gtid; t < ntrips; t += nthreads) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = xv[t * U + u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cast4(w[u], t * U + u);
   }
-  for (int64_t i = n8 * 8 + gtid; i < n; i += nthreads) y[i] = (uint16_t)f32_to_bf16_rne(x[i]);
+  for (int64_t i = ntrips * U + gtid; i < nv; i += nthreads) cast4(xv[i], i);
+  for (int64_t e = nv * 4 + gtid; e < n; e += nthreads) y[e] = (uint16_t)f32_to_bf16_rne(x[e]);
 }
 
 static int stream_grid(int64_t n) {
-  // enough workgroups to cover all 256 CUs several times over, capped by the work
-  const int64_t per_block = (int64_t)QTHREADS * 8 * 4;
+  // up to 16 workgroups per CU, each running several trips
+  const int64_t per_block = (int64_t)QTHREADS * kVecsInFlight * 4;  // elements (fp32 vectors)
   int64_t g = (n + per_block - 1) / per_block;
   if (g > 256 * 16) g = 256 * 16;
   if (g < 1) g = 1;
