@@ -58,19 +58,14 @@ struct FwdParams {
   int xcd_remap;
 };
 
-template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_, bool PINGPONG_ = false, int INWAVE_WAVES_ = 4>
+template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_>
 struct FwdCfg {
   static constexpr bool FP8 = FP8_;
   static constexpr int DQK = DQK_, DV = DV_, BN = BN_;
-  // Schedule. In-wave (PINGPONG false): 4-wave workgroups, two per CU; each
-  // wave interleaves its MFMAs with its softmax. Ping-pong: one 8-wave
-  // workgroup per CU; waves w and w+4 share a SIMD, and the two halves of
-  // the workgroup alternate between a matrix phase (all MFMAs of a step)
-  // and a vector phase (the softmax of a step), one phase apart.
-  static constexpr bool PINGPONG = PINGPONG_;
-  static constexpr int NWAVES = PINGPONG ? 8 : INWAVE_WAVES_;
-  static constexpr int WG_PER_CU = 8 / NWAVES;       // two waves per SIMD
-  static_assert(NWAVES == 4 || NWAVES == 8, "waves per workgroup");
+  // 4-wave workgroups, two per CU (two waves per SIMD); each wave
+  // interleaves its MFMAs with its own softmax
+  static constexpr int NWAVES = 4;
+  static constexpr int WG_PER_CU = 2;
   static constexpr int BM = 32 * NWAVES;             // query rows per workgroup
   static constexpr int NTHREADS = NWAVES * 64;
   static constexpr int EB = FP8 ? 1 : 2;             // bytes per element
@@ -81,7 +76,7 @@ struct FwdCfg {
   static constexpr int KTILE = BN * KROW;
   static constexpr int VTILE = BN * VROW;
   static constexpr int NSTAGE = NSTAGE_;             // K ring and V ring depth
-  static constexpr int LOOKAHEAD = 2;                // MFMA jobs whose LDS operand reads are in flight
+  static constexpr int LOOKAHEAD = FP8 ? 2 : 1;      // MFMA jobs whose LDS operand reads are in flight
   // folded score form available (the scaled MFMA exists for FP8 only)
   static constexpr bool FOLDABLE = FP8;
   static constexpr int LDS_BYTES = NSTAGE * (KTILE + VTILE);
@@ -93,14 +88,12 @@ struct FwdCfg {
   static constexpr int NQK = NST * QK_STEPS;                 // Q.K^T MFMAs per step
   static constexpr int KLOADS = KTILE / 16 / NTHREADS;       // 16-byte loads per lane per tile
   static constexpr int VLOADS = VTILE / 16 / NTHREADS;
-  // loads a wave may leave in flight at the end of a step (in-wave) or of a
-  // phase (ping-pong: the tile a matrix phase reads was loaded NSTAGE steps
-  // earlier and must be complete three phases before)
-  static constexpr int INFLIGHT = (NSTAGE - (PINGPONG ? 3 : 2)) * (KLOADS + VLOADS);
+  // loads a wave may leave in flight at the end of a step
+  static constexpr int INFLIGHT = (NSTAGE - 2) * (KLOADS + VLOADS);
   static_assert((FP8 ? BN == 64 : (BN == 32 || BN == 64)), "FP8: 64 keys per step (one P operand); BF16: 32 or 64");
   static_assert(DV % 32 == 0 && DQK % 64 == 0, "head dims");
   static_assert(KTILE % (16 * NTHREADS) == 0 && VTILE % (16 * NTHREADS) == 0, "staging split");
-  static_assert(NSTAGE >= (PINGPONG ? 4 : 2) && INFLIGHT < 64, "ring depth / vmcnt range");
+  static_assert(NSTAGE >= 2 && INFLIGHT < 64, "ring depth / vmcnt range");
   static_assert(WG_PER_CU * LDS_BYTES <= 160 * 1024, "LDS of the workgroups of one CU");
 };
 
@@ -403,13 +396,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
           a[2 * rr + 1] = x[1];
         }
       } else {
-        i16x4 x[2];
-#pragma unroll
-        for (int hp = 0; hp < 2; ++hp) x[hp] = lds_read_tr16(vl + (16 * u + 8 * hp) * C::VROW + v_off[tv]);
-        a[0] = (int)(uint16_t)x[0][0] | ((int)(uint16_t)x[0][1] << 16);
-        a[1] = (int)(uint16_t)x[0][2] | ((int)(uint16_t)x[0][3] << 16);
-        a[2] = (int)(uint16_t)x[1][0] | ((int)(uint16_t)x[1][1] << 16);
-        a[3] = (int)(uint16_t)x[1][2] | ((int)(uint16_t)x[1][3] << 16);
+        // two transposed reads of 4 elements each, concatenated (element e
+        // of the operand is 16-bit lane e of the pair)
+        const i32x2 x0 = __builtin_bit_cast(i32x2, lds_read_tr16(vl + (16 * u) * C::VROW + v_off[tv]));
+        const i32x2 x1 = __builtin_bit_cast(i32x2, lds_read_tr16(vl + (16 * u + 8) * C::VROW + v_off[tv]));
+        a = i32x4{x0[0], x0[1], x1[0], x1[1]};
       }
     } else {
       const int jq = j - C::NPV, t = jq % C::NST, u = jq / C::NST;
@@ -540,6 +531,14 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   };
 
   constexpr int NJOB = C::NPV + C::NQK;
+  // Issue order of the step's jobs (job numbers: P.V 0..NPV-1, Q.K^T
+  // NPV..NJOB-1). With one score tile per step (BF16) every Q.K^T job
+  // accumulates into the same tile, so P.V and Q.K^T jobs alternate to keep
+  // two dependent MFMAs apart; otherwise P.V jobs come first.
+  constexpr bool ALTERNATE = C::NST == 1 && C::NPV == C::NQK;
+  auto job_at = [](int pos) constexpr -> int {
+    return ALTERNATE ? ((pos & 1) ? C::NPV + (pos >> 1) : (pos >> 1)) : pos;
+  };
   // ---- one pipeline step n with parity P (tile n's scores in sbuf[P])
   auto step = [&](int n, auto Pc) {
     constexpr int P = decltype(Pc)::value, Q = 1 - P;
@@ -569,15 +568,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     int reads0 = 0;
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
-      fr[j] = load_frag(j, vl, kl);
-      reads0 += frag_reads(j);
+      fr[j] = load_frag(job_at(j), vl, kl);
+      reads0 += frag_reads(job_at(j));
     }
     sched_group<kSchedDsRead>(reads0);
     int c = 0;
 #pragma unroll
     for (int j = 0; j < NJOB; ++j) {
-      if (j + LA < NJOB) fr[(j + LA) % (LA + 1)] = load_frag(j + LA, vl, kl);
-      run_job(j, fr[j % (LA + 1)], std::integral_constant<int, Q>{}, std::integral_constant<int, Q>{});
+      if (j + LA < NJOB) fr[(j + LA) % (LA + 1)] = load_frag(job_at(j + LA), vl, kl);
+      run_job(job_at(j), fr[j % (LA + 1)], std::integral_constant<int, Q>{}, std::integral_constant<int, Q>{});
       // this step's loads (K(n+NS), V(n+NS-2)) go out behind the first MFMA,
       // so their address arithmetic overlaps the softmax
       if (j == 0) {
@@ -586,39 +585,26 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       }
       // chunks are spread over all but the last two jobs, so the row-sum
       // chain is complete (for the lazy-max check below) by the time the
-      // last MFMAs have issued (ping-pong: the softmax has its own phase)
-      if constexpr (!C::PINGPONG) {
-        const int c_end = j + 2 >= NJOB ? NCHUNK : (j + 1) * NCHUNK / (NJOB - 2);
-        for (; c < c_end; ++c) probs_chunk(c, Pc, m_run, lsum, False_{});
-      }
+      // last MFMAs have issued
+      const int c_end = j + 2 >= NJOB ? NCHUNK : (j + 1) * NCHUNK / (NJOB - 2);
+      for (; c < c_end; ++c) probs_chunk(c, Pc, m_run, lsum, False_{});
       // issue order: this job's look-ahead reads, then its MFMA; the softmax
       // instructions are left to the scheduler (pinning them measured slower)
       if constexpr (FOLD) {
         // the scaled MFMA is not matched by scheduling groups: fence each job
-        // (in-wave schedule; a matrix phase has nothing to interleave)
-        if constexpr (!C::PINGPONG) sched_fence();
+        sched_fence();
       } else {
-        if (j + LA < NJOB) sched_group<kSchedDsRead>(frag_reads(j + LA));
+        if (j + LA < NJOB) sched_group<kSchedDsRead>(frag_reads(job_at(j + LA)));
         sched_group<kSchedMfma>(1);
       }
     }
     wait_vmcnt<C::INFLIGHT>();
     __syncthreads();
-    if constexpr (C::PINGPONG) {
-      // vector phase: the softmax of tile n while the other half of the
-      // workgroup runs its matrix phase
-#pragma unroll
-      for (int cc = 0; cc < NCHUNK; ++cc) probs_chunk(cc, Pc, m_run, lsum, False_{});
-    }
-    // lazy-max check of tile n, by when its row sums are complete (the exact
-    // path touches registers only)
+    // lazy-max check of tile n after the barrier, by when its row sums are
+    // complete (the exact path touches registers only)
     const bool first = FOLD && n == 0;
     if (wave_any(first | !(lsum <= kLazyMaxThreshold))) exact_path(Pc, lsum, first);
     l_run += lsum;
-    if constexpr (C::PINGPONG) {
-      wait_vmcnt<C::INFLIGHT>();
-      __syncthreads();
-    }
   };
 
   // ---- prologue: stages of K(0..NS-1) and V(0..NS-3) in flight, then all
@@ -640,18 +626,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // loaded meanwhile (their stages were last read in step n-1). At the end
   // each wave waits for all but the last NS-2 steps' loads, so K(n+2) and
   // V(n) are complete at the barrier.
-  // Ping-pong: the upper half of the workgroup starts one phase late (an
-  // extra barrier before its first step, matched by one after the lower
-  // half's last step), so at every barrier interval one wave of each SIMD is
-  // in its matrix phase and the other in its vector phase.
-  const bool upper_half = C::PINGPONG && wave >= C::NWAVES / 2;
-  if (upper_half) __syncthreads();
   for (int n = 0; n < T; n += 2) {
     step(n, std::integral_constant<int, 0>{});
     if (n + 1 >= T) break;
     step(n + 1, std::integral_constant<int, 1>{});
   }
-  if (C::PINGPONG && !upper_half) __syncthreads();
   // last tile T-1: its lazy-max check, then its P.V (V stage complete: waited
   // at the end of step T-2)
   {
