@@ -583,10 +583,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
         issue_k(n + NS);
         issue_v(n + NS - 2);
       }
-      // chunks are spread over all but the last two jobs, so the row-sum
-      // chain is complete (for the lazy-max check below) by the time the
-      // last MFMAs have issued
-      const int c_end = j + 2 >= NJOB ? NCHUNK : (j + 1) * NCHUNK / (NJOB - 2);
+      // chunks are spread evenly over the jobs (the last one follows the
+      // last MFMA; the lazy-max check waits at the barrier anyway)
+      const int c_end = (j + 1) * NCHUNK / NJOB;
       for (; c < c_end; ++c) probs_chunk(c, Pc, m_run, lsum, False_{});
       // issue order: this job's look-ahead reads, then its MFMA; the softmax
       // instructions are left to the scheduler (pinning them measured slower)

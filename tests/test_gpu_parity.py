@@ -54,6 +54,9 @@ SMALL = [
     Workload("tiny_mha_fp8", 1, 512, 2, 2, 128, 128, "fp8", "gauss"),
     Workload("ragged_gqa_fp8_outlier", 1, 777, 8, 2, 128, 128, "fp8", "outlier"),
     Workload("batch2_gqa_fp8", 2, 300, 4, 1, 128, 128, "fp8", "gauss"),
+    # B * Hkv = 8: the XCD-aware work order (whole kv units per XCD) is used
+    Workload("batch2_xcd_order_fp8", 2, 200, 8, 4, 128, 128, "fp8", "outlier"),
+    Workload("batch4_xcd_order_bf16", 4, 100, 4, 2, 128, 128, "bf16", "gauss"),
     Workload("single_row_fp8", 1, 1, 2, 2, 128, 128, "fp8", "gauss"),
     Workload("ragged_mla_fp8", 1, 333, 4, 4, 192, 128, "fp8", "mla"),
     Workload("ragged_gqa_bf16", 1, 333, 8, 2, 128, 128, "bf16", "gauss"),
