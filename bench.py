@@ -102,7 +102,7 @@ def _amd_smi_sample(smi: str):
         return None
 
 
-def sustained(seconds: float, attention, flops: float, stream) -> dict:
+def sustained(seconds: float, attention, flops: float, stream, peak_tflops: float) -> dict:
     """Back-to-back attention launches for `seconds`, with SCLK and power sampled meanwhile.
 
     The pages report that the clock depends on the data (bit toggling), so the
@@ -156,6 +156,9 @@ def sustained(seconds: float, attention, flops: float, stream) -> dict:
         mean_clk = np.array([x[0] for x in samples])
         rec["sclk_mhz"] = {"median": round(float(np.median(mean_clk)), 1), "min": round(float(mean_clk.min()), 1),
                            "max": round(float(mean_clk.max()), 1), "samples": len(samples)}
+        # the dense peak scales with the clock (2.4 GHz for the datasheet figure)
+        rec["frac_of_peak_at_measured_sclk"] = round(
+            rec["attention_tflops"] / (peak_tflops * float(np.median(mean_clk)) / 2400.0), 4)
         pws = [x[2] for x in samples if x[2] is not None]
         if pws:
             rec["socket_power_w"] = {"median": float(np.median(pws)), "max": float(max(pws))}
@@ -345,7 +348,7 @@ def main(argv=None) -> int:
     }
     if args.sustain_s > 0:
         print(f"# sustained run: {args.sustain_s:g} s of attention launches", file=sys.stderr, flush=True)
-        rec["sustained"] = sustained(args.sustain_s, attention, flops, stream)
+        rec["sustained"] = sustained(args.sustain_s, attention, flops, stream, peak)
     else:
         rec["sustained"] = None
     if not args.no_cpu_baseline:
