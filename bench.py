@@ -22,6 +22,7 @@ Only one GPU is used: ``--gpus`` above 1 exits with an error.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import math
 import hashlib
 import json
@@ -162,6 +163,8 @@ def sustained(seconds: float, attention, flops: float, stream, peak_tflops: floa
         pws = [x[2] for x in samples if x[2] is not None]
         if pws:
             rec["socket_power_w"] = {"median": float(np.median(pws)), "max": float(max(pws))}
+            # whole-socket energy (HBM and idle parts included) per unit of work
+            rec["tflop_per_joule"] = round(rec["attention_tflops"] / float(np.median(pws)), 4)
     return rec
 
 
@@ -202,6 +205,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dist", choices=("gauss", "outlier", "mla"), default=None,
+                    help="override the workload's input distribution (same shape), e.g. to compare the "
+                         "clock and energy of Gaussian and heavy-tailed inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--sustain-s", type=float, default=10.0,
                     help="seconds of back-to-back attention launches with SCLK sampling (0 = skip)")
@@ -228,6 +234,9 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU (none visible)", file=sys.stderr)
         return 2
     w = WORKLOADS[args.workload]
+    default_dist = w.dist
+    if args.dist is not None:
+        w = dataclasses.replace(w, dist=args.dist)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"# workload {w.name}: generating inputs (seed {args.seed})", file=sys.stderr, flush=True)
@@ -307,7 +316,8 @@ def main(argv=None) -> int:
         del src, dst
 
     src_hash = kernel_source_hash()
-    traffic = traffic_from_profile(w.name, src_hash)
+    # HBM traffic does not depend on the values, but the profile names its inputs
+    traffic = traffic_from_profile(w.name, src_hash) if w.dist == default_dist else None
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
