@@ -12,13 +12,19 @@ Distributions:
   multiplied by 8. The 4 channels are drawn independently for each tensor
   and each head. This stands in for the captured Mistral-7B / Qwen3-8B
   layers the pages measure on, whose weights are not available.
+* ``outlier_shared`` -- as ``outlier``, but the 4 channels are drawn once per
+  kv head and scaled in K's head and in each query head of its group, so
+  the large channels of Q and K coincide, as in real activations whose
+  outlier features sit in fixed channels. Then a few products dominate each
+  score. This is the case a Hadamard rotation of Q and K is for.
 * ``mla``     -- V ~ N(0, 1); Q and K ~ N(0, 1) on the 128 no-rope dims and
   N(0, 2) (std sqrt 2) on dims 128..191, the rope part of the
   DeepSeek-V2-Lite-shaped 192/128 head.
 
 Generator: numpy PCG64 via ``default_rng([seed, tensor_index])``, tensor
 index 0/1/2 for Q/K/V; outlier channels come from the same generator after
-the tensor's values.
+the tensor's values (``outlier``) or, shared, from ``default_rng([seed, 3])``
+with one draw per kv head (``outlier_shared``).
 """
 
 from __future__ import annotations
@@ -38,7 +44,7 @@ class Workload:
     d_qk: int
     d_v: int
     dtype: str        # "fp8" or "bf16"
-    dist: str         # "gauss", "outlier" or "mla"
+    dist: str         # "gauss", "outlier", "outlier_shared" or "mla"
     causal: bool = True
 
     def as_dict(self):
@@ -89,4 +95,12 @@ def make_inputs(w: Workload | str, seed: int = 0, **overrides):
     q = _draw(seed, 0, (w.B, w.S, w.Hq, w.d_qk), w.dist, "q")
     k = _draw(seed, 1, (w.B, w.S, w.Hkv, w.d_qk), w.dist, "k")
     v = _draw(seed, 2, (w.B, w.S, w.Hkv, w.d_v), w.dist, "v")
+    if w.dist == "outlier_shared":
+        rng = np.random.default_rng([seed, 3])
+        G = w.Hq // w.Hkv
+        for g in range(w.Hkv):
+            ch = rng.choice(w.d_qk, 4, replace=False)
+            k[:, :, g, ch] *= np.float32(8.0)
+            for h in range(g * G, (g + 1) * G):
+                q[:, :, h, ch] *= np.float32(8.0)
     return q, k, v

@@ -27,10 +27,15 @@ Modules:
 * ``attention`` -- exact causal softmax attention in float64 on dequantized
   inputs: O and the natural-log log-sum-exp, for whole tensors or for
   selected rows.
+* ``rotation``  -- the Hadamard rotation of Q and K ahead of the FP8 cast
+  (aicronaca.it, section "Perché l'FP8 non basta da solo").
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (format tables against torch's casts and the pages' +8-per-doubling fact;
-attention against brute force, closed forms and invariants).
+attention against brute force, closed forms and invariants) and
+``tests/test_oracle_rotation.py`` (Hadamard matrices against scipy and the
+closed form, rotation against a brute force, a hand-worked one-hot case,
+score invariance and the page's error claim).
 """
 
 from .formats import (

@@ -35,6 +35,7 @@ import math
 
 import numpy as np
 
+from .rotation import hadamard_encode, hadamard_scales
 from .formats import (bf16_decode, bf16_encode, dequantize_fp8, encode_with_scale, per_tensor_scale,
                       per_tensor_scale_folded)
 
@@ -166,13 +167,35 @@ class _QuantizedView:
         return bf16_decode(c)
 
 
+class _RotatedView(_QuantizedView):
+    """As _QuantizedView for a Hadamard-rotated FP8 tensor (oracle/rotation.py).
+
+    Codes come from the rotated rows with the code scale; indexing returns
+    decode(code) * stored scale. Indices must keep the last axis whole (rows
+    are rotated one head vector at a time).
+    """
+
+    def __init__(self, x32, code_scale, stored_scale):
+        self.x32 = np.asarray(x32, dtype=np.float32)
+        self.kind = "fp8"
+        self.shape = self.x32.shape
+        self.code_scale = np.float32(code_scale)
+        self.scale = np.float32(stored_scale)
+
+    def codes(self, idx=slice(None)):
+        return hadamard_encode(self.x32[idx], self.code_scale)
+
+
 def prefill_reference(q32, k32, v32, dtype: str, causal: bool = True, rows=None,
-                      softmax_scale: float | None = None, fold_q: bool = False):
+                      softmax_scale: float | None = None, fold_q: bool = False, hadamard: bool = False):
     """The whole path on float32 inputs: the input step, then attention.
 
     dtype "fp8": per-tensor absmax e4m3fn codes and scales (with ``fold_q``
     the query takes the folded scale for the key scale and softmax scale);
     "bf16": bf16 RNE.
+    With ``hadamard`` (fp8 only, implies ``fold_q``) Q and K are rotated
+    before quantization (oracle/rotation.py); the key keeps its plain scale
+    and the query's stored scale is its folded scale over the block size.
     Attention runs in float64 on the dequantized values. Without ``rows``:
     returns the codes (uint8 for fp8, uint16 bit patterns for bf16), the
     scales (1.0 for bf16) and the full O / LSE. With ``rows`` (a list of
@@ -181,12 +204,19 @@ def prefill_reference(q32, k32, v32, dtype: str, causal: bool = True, rows=None,
     """
     if dtype not in ("fp8", "bf16"):
         raise ValueError("dtype must be 'fp8' or 'bf16'")
-    kv = [_QuantizedView(t, dtype) for t in (k32, v32)]
-    q_scale = None
-    if dtype == "fp8" and fold_q:
-        sm = 1.0 / math.sqrt(np.shape(q32)[-1]) if softmax_scale is None else softmax_scale
-        q_scale = per_tensor_scale_folded(q32, kv[0].scale, sm)
-    views = [_QuantizedView(q32, dtype, q_scale)] + kv
+    sm = 1.0 / math.sqrt(np.shape(q32)[-1]) if softmax_scale is None else softmax_scale
+    if hadamard:
+        if dtype != "fp8":
+            raise ValueError("the Hadamard rotation applies to the fp8 path")
+        kcs, ks = hadamard_scales(k32)
+        qcs, qs = hadamard_scales(q32, k_scale=ks, softmax_scale=sm)
+        views = [_RotatedView(q32, qcs, qs), _RotatedView(k32, kcs, ks), _QuantizedView(v32, dtype)]
+    else:
+        kv = [_QuantizedView(t, dtype) for t in (k32, v32)]
+        q_scale = None
+        if dtype == "fp8" and fold_q:
+            q_scale = per_tensor_scale_folded(q32, kv[0].scale, sm)
+        views = [_QuantizedView(q32, dtype, q_scale)] + kv
     out = dict(q_scale=views[0].scale, k_scale=views[1].scale, v_scale=views[2].scale, views=views)
     if rows is None:
         qc, kc, vc = (vw.codes() for vw in views)
