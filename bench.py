@@ -205,7 +205,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--dist", choices=("gauss", "outlier", "mla"), default=None,
+    ap.add_argument("--hadamard", action="store_true",
+                    help="FP8: rotate Q and K by Hadamard blocks in the input step (attn_quantize_fp8_hadamard)")
+    ap.add_argument("--dist", choices=("gauss", "outlier", "outlier_shared", "mla"), default=None,
                     help="override the workload's input distribution (same shape), e.g. to compare the "
                          "clock and energy of Gaussian and heavy-tailed inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
@@ -255,13 +257,18 @@ def main(argv=None) -> int:
 
     sm_scale = 1.0 / math.sqrt(w.d_qk)
 
+    if args.hadamard and w.dtype != "fp8":
+        print("--hadamard applies to FP8 workloads only", file=sys.stderr)
+        return 2
+
     def input_step():
         if w.dtype == "fp8":
             # K and V first: the query's folded scale is derived from K's
             for i in (1, 2):
-                ops.attn_quantize_fp8((q32, k32, v32)[i], out=codes[i], scale=scales[i:i + 1], stream=stream)
+                ops.attn_quantize_fp8((q32, k32, v32)[i], out=codes[i], scale=scales[i:i + 1], stream=stream,
+                                      hadamard=args.hadamard and i == 1)
             ops.attn_quantize_fp8(q32, out=codes[0], scale=scales[0:1], stream=stream, k_scale=scales[1:2],
-                                  softmax_scale=sm_scale)
+                                  softmax_scale=sm_scale, hadamard=args.hadamard)
         else:
             for i, t in enumerate((q32, k32, v32)):
                 ops.attn_cast_bf16(t, out=codes[i], stream=stream)
@@ -333,6 +340,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "d_qk": w.d_qk,
                    "d_v": w.d_v, "causal": w.causal, "dist": w.dist, "seed": args.seed,
+                   "hadamard": bool(args.hadamard),
                    "step": "input step (quantize/cast Q,K,V) + attention"},
         "attention_ms": round(attn_avg, 4),
         "attention_ms_min": round(float(np.min(attn_ms)), 4),

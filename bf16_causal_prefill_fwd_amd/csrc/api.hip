@@ -124,8 +124,9 @@ int attn_prefill_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
 
 namespace {
 
+// block: 0 = no rotation, else the Hadamard block size (64 or 128)
 int quantize_impl(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, const float* d_k_scale,
-                  float softmax_scale, hipStream_t stream) {
+                  float softmax_scale, int block, hipStream_t stream) {
   if (!x || !x8 || !d_scale) return ATTN_ERR_INVALID;
   if (n <= 0 || n >= ((int64_t)1 << 40)) return ATTN_ERR_INVALID;
   if (x_dtype != 0 && x_dtype != 1) return ATTN_ERR_UNSUPPORTED;
@@ -143,21 +144,30 @@ int quantize_impl(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_s
   }
   const int ready = attn::device_ready();
   if (ready != ATTN_OK) return ready;
-  return attn::launch_quantize_fp8(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, stream) == hipSuccess
-             ? ATTN_OK
-             : ATTN_ERR_HIP;
+  const hipError_t e =
+      block ? attn::launch_quantize_fp8_hadamard(x, x_dtype, n, block, x8, d_scale, d_k_scale, softmax_scale, stream)
+            : attn::launch_quantize_fp8(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 }  // namespace
 
 int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, hipStream_t stream) {
-  return quantize_impl(x, x_dtype, n, x8, d_scale, nullptr, 0.f, stream);
+  return quantize_impl(x, x_dtype, n, x8, d_scale, nullptr, 0.f, 0, stream);
 }
 
 int attn_quantize_fp8_q(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, const float* d_k_scale,
                         float softmax_scale, hipStream_t stream) {
   if (!d_k_scale) return ATTN_ERR_INVALID;
-  return quantize_impl(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, stream);
+  return quantize_impl(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, 0, stream);
+}
+
+int attn_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, int d, uint8_t* x8, float* d_scale,
+                               const float* d_k_scale, float softmax_scale, hipStream_t stream) {
+  if (d <= 0 || n <= 0 || n % d != 0) return ATTN_ERR_INVALID;
+  const int block = (d & -d) < 128 ? (d & -d) : 128;
+  if (block != 64 && block != 128) return ATTN_ERR_UNSUPPORTED;
+  return quantize_impl(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, block, stream);
 }
 
 int attn_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream) {

@@ -10,6 +10,11 @@ namespace attn {
 // for that key scale and softmax scale.
 hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
                                const float* d_k_scale, float sm_scale, hipStream_t stream);
+// Hadamard-rotated variant: block = 64 or 128 columns, n a multiple of it.
+// d_k_scale == nullptr: key (plain scale); else query (folded scale / block).
+hipError_t launch_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, int block, uint8_t* x8,
+                                        float* d_scale, const float* d_k_scale, float sm_scale,
+                                        hipStream_t stream);
 hipError_t launch_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream);
 
 }  // namespace attn

@@ -159,8 +159,154 @@ __global__ __launch_bounds__(QTHREADS) void quant_kernel(const void* __restrict_
     out[e] = (uint8_t)(cvt_fp8x2(__fdiv_rn(In16<XDT>::load1(x, e), scale), 0.f, 0, false) & 0xFF);
 }
 
-__global__ void scale_finalize_kernel(uint32_t* amax_bits, const float* d_k_scale, float sm_scale) {
-  *amax_bits = __float_as_uint(quant_scale(*amax_bits, d_k_scale, sm_scale));
+// Replaces the absmax bits by the stored scale: the scale the codes were
+// taken with, times `post` (1, or 1/b for a rotated query: exact, b is a
+// power of two).
+__global__ void scale_finalize_kernel(uint32_t* amax_bits, const float* d_k_scale, float sm_scale, float post) {
+  *amax_bits = __float_as_uint(quant_scale(*amax_bits, d_k_scale, sm_scale) * post);
+}
+
+// ---- Hadamard rotation ahead of the FP8 cast (aicronaca.it, section "Perché
+// l'FP8 non basta da solo": rotating Q and K before the cast about halves the
+// input error). Each b-column block of a row (b = 128 for d = 128, 64 for
+// d = 192) becomes y = x H_b, H_b the unnormalized Sylvester matrix with
+// entry (i, j) = (-1)^popcount(i & j), so (q H)(k H)^T = b q.k^T. The sums
+// are formed in fp64, so the code decision is taken on (nearly) exact values:
+// code = e4m3(fp32(y * fp64(1 / scale))). The absmax is taken over fp32(|y|)
+// and the scale follows the unrotated rules; a query's stored scale is then
+// divided by b.
+//
+// Lane layout: one block row per quad of lanes. Lane j of a quad holds the
+// row's 16-byte input vectors j, j+4, j+8, ..., so one load instruction of a
+// quad reads 64 contiguous bytes. Element e of the row sits in lane
+// j = (e / R) % 4, register (e % R) + R * (e / 4R), R elements per vector.
+// The two lane bits of e are exchanged with quad-permute DPP moves; the
+// other bits are butterflies over the lane's own registers.
+template <int XDT, int BLK>
+struct HadShape {
+  static constexpr int R = XDT == 0 ? 4 : 8;   // elements per 16-byte vector
+  static constexpr int NV = BLK / (4 * R);     // vectors per lane
+  static constexpr int NE = NV * R;            // elements per lane
+  static_assert(NV >= 1 && BLK % (4 * R) == 0, "block layout");
+};
+
+// Value of `v` in lane (lane ^ M) of the same quad (M = 1 or 2).
+template <int M>
+__device__ __forceinline__ double quad_xor(double v) {
+  constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const uint64_t u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, ctrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), ctrl, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// Rotated values of this lane's elements of block row `br` (all zero when
+// br >= nbr, which holds for a whole quad at once). Every lane of the wave
+// must call it (the DPP moves read the quad's other lanes).
+template <int XDT, int BLK>
+__device__ __forceinline__ void had_rotate(const void* __restrict__ x, int64_t br, int64_t nbr, int j, double* y) {
+  using H = HadShape<XDT, BLK>;
+  uint4 w[H::NV];
+  if (br < nbr) {
+    const uint4* row = (const uint4*)((const char*)x + br * (int64_t)(BLK * (XDT == 0 ? 4 : 2)));
+#pragma unroll
+    for (int u = 0; u < H::NV; ++u) w[u] = row[j + 4 * u];
+  } else {
+#pragma unroll
+    for (int u = 0; u < H::NV; ++u) w[u] = make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < H::NV; ++u) {
+    float f[H::R];
+    In16<XDT>::unpack(w[u], f);
+#pragma unroll
+    for (int r = 0; r < H::R; ++r) y[u * H::R + r] = (double)f[r];
+  }
+  // index bits held within the lane: (a, b) -> (a + b, a - b), a at the
+  // position with the bit clear
+#pragma unroll
+  for (int h = 1; h < H::NE; h <<= 1) {
+#pragma unroll
+    for (int t = 0; t < H::NE; ++t) {
+      if (!(t & h)) {
+        const double a = y[t], b = y[t + h];
+        y[t] = a + b;
+        y[t + h] = a - b;
+      }
+    }
+  }
+  // the two lane bits
+#pragma unroll
+  for (int t = 0; t < H::NE; ++t) {
+    const double o = quad_xor<1>(y[t]);
+    y[t] = (j & 1) ? o - y[t] : y[t] + o;
+  }
+#pragma unroll
+  for (int t = 0; t < H::NE; ++t) {
+    const double o = quad_xor<2>(y[t]);
+    y[t] = (j & 2) ? o - y[t] : y[t] + o;
+  }
+}
+
+// Each wave takes 16 block rows per trip; the trip count is uniform per wave.
+template <int XDT, int BLK>
+__global__ __launch_bounds__(QTHREADS) void had_amax_kernel(const void* __restrict__ x, int64_t nbr,
+                                                             uint32_t* amax_bits) {
+  using H = HadShape<XDT, BLK>;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (QTHREADS / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (QTHREADS / 64);
+  float m = 0.f;
+  for (int64_t br0 = wave * 16; br0 < nbr; br0 += nwaves * 16) {
+    double y[H::NE];
+    had_rotate<XDT, BLK>(x, br0 + (lane >> 2), nbr, lane & 3, y);
+#pragma unroll
+    for (int t = 0; t < H::NE; ++t) m = fmaxf(m, (float)fabs(y[t]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float red[QTHREADS / 64];
+  if (lane == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < QTHREADS / 64; ++w) r = fmaxf(r, red[w]);
+    atomicMax(amax_bits, __float_as_uint(r));
+  }
+}
+
+template <int XDT, int BLK>
+__global__ __launch_bounds__(QTHREADS) void had_quant_kernel(const void* __restrict__ x, int64_t nbr,
+                                                              const uint32_t* __restrict__ amax_bits,
+                                                              const float* __restrict__ d_k_scale, float sm_scale,
+                                                              uint8_t* __restrict__ out) {
+  using H = HadShape<XDT, BLK>;
+  const double rcp = 1.0 / (double)quant_scale(*amax_bits, d_k_scale, sm_scale);
+  const int lane = threadIdx.x & 63, j = lane & 3;
+  const int64_t wave = (int64_t)blockIdx.x * (QTHREADS / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (QTHREADS / 64);
+  for (int64_t br0 = wave * 16; br0 < nbr; br0 += nwaves * 16) {
+    const int64_t br = br0 + (lane >> 2);
+    double y[H::NE];
+    had_rotate<XDT, BLK>(x, br, nbr, j, y);
+    if (br < nbr) {
+      uint8_t* orow = out + br * BLK;
+#pragma unroll
+      for (int u = 0; u < H::NV; ++u) {
+        int c[H::R / 4];
+#pragma unroll
+        for (int q = 0; q < H::R / 4; ++q) {
+          const double* yy = y + u * H::R + 4 * q;
+          const int lo = cvt_fp8x2((float)(yy[0] * rcp), (float)(yy[1] * rcp), 0, false);
+          c[q] = cvt_fp8x2((float)(yy[2] * rcp), (float)(yy[3] * rcp), lo, true);
+        }
+        uint8_t* dst = orow + H::R * (j + 4 * u);
+        if constexpr (H::R == 4) *(uint32_t*)dst = (uint32_t)c[0];
+        else *(uint2*)dst = make_uint2((uint32_t)c[0], (uint32_t)c[1]);
+      }
+    }
+  }
 }
 
 // fp32 -> bf16, round to nearest even (finite inputs).
@@ -214,7 +360,37 @@ hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x
     hipLaunchKernelGGL(amax_kernel<1>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits);
     hipLaunchKernelGGL(quant_kernel<1>, dim3(grid), dim3(QTHREADS), 0, stream, x, n, bits, d_k_scale, sm_scale, x8);
   }
-  hipLaunchKernelGGL(scale_finalize_kernel, dim3(1), dim3(1), 0, stream, bits, d_k_scale, sm_scale);
+  hipLaunchKernelGGL(scale_finalize_kernel, dim3(1), dim3(1), 0, stream, bits, d_k_scale, sm_scale, 1.0f);
+  return hipGetLastError();
+}
+
+template <int XDT, int BLK>
+static void launch_had(const void* x, int64_t nbr, uint32_t* bits, const float* d_k_scale, float sm_scale,
+                       uint8_t* x8, hipStream_t stream) {
+  // 64 block rows per workgroup trip (16 per wave), up to 16 workgroups per CU
+  int64_t g = (nbr + 63) / 64;
+  if (g > 256 * 16) g = 256 * 16;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL((had_amax_kernel<XDT, BLK>), dim3((int)g), dim3(QTHREADS), 0, stream, x, nbr, bits);
+  hipLaunchKernelGGL((had_quant_kernel<XDT, BLK>), dim3((int)g), dim3(QTHREADS), 0, stream, x, nbr, bits, d_k_scale,
+                     sm_scale, x8);
+}
+
+hipError_t launch_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, int block, uint8_t* x8,
+                                        float* d_scale, const float* d_k_scale, float sm_scale,
+                                        hipStream_t stream) {
+  uint32_t* bits = (uint32_t*)d_scale;
+  const int64_t nbr = n / block;
+  hipLaunchKernelGGL(amax_reset_kernel, dim3(1), dim3(1), 0, stream, bits);
+  if (block == 128) {
+    if (x_dtype == 0) launch_had<0, 128>(x, nbr, bits, d_k_scale, sm_scale, x8, stream);
+    else launch_had<1, 128>(x, nbr, bits, d_k_scale, sm_scale, x8, stream);
+  } else {
+    if (x_dtype == 0) launch_had<0, 64>(x, nbr, bits, d_k_scale, sm_scale, x8, stream);
+    else launch_had<1, 64>(x, nbr, bits, d_k_scale, sm_scale, x8, stream);
+  }
+  const float post = d_k_scale ? 1.0f / (float)block : 1.0f;
+  hipLaunchKernelGGL(scale_finalize_kernel, dim3(1), dim3(1), 0, stream, bits, d_k_scale, sm_scale, post);
   return hipGetLastError();
 }
 

@@ -40,6 +40,8 @@ _SIGNATURES = {
     "attn_quantize_fp8": (_c_int, [_c_void_p, _c_int, _c_int64, _c_void_p, _c_void_p, _c_void_p]),
     "attn_quantize_fp8_q": (_c_int, [_c_void_p, _c_int, _c_int64, _c_void_p, _c_void_p, _c_void_p, _c_float,
                                      _c_void_p]),
+    "attn_quantize_fp8_hadamard": (_c_int, [_c_void_p, _c_int, _c_int64, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                            _c_float, _c_void_p]),
     "attn_cast_bf16": (_c_int, [_c_void_p, _c_int64, _c_void_p, _c_void_p]),
     "attn_strerror": (ctypes.c_char_p, [_c_int]),
     "attn_abi_version": (_c_int, []),
@@ -100,12 +102,15 @@ def _need(t: torch.Tensor, name: str):
 
 
 def attn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None, scale: torch.Tensor | None = None,
-                      stream=None, k_scale: torch.Tensor | None = None, softmax_scale: float | None = None):
+                      stream=None, k_scale: torch.Tensor | None = None, softmax_scale: float | None = None,
+                      hadamard: bool = False):
     """Per-tensor e4m3fn quantization on the device.
 
     With ``k_scale`` (the key tensor's device scale) and ``softmax_scale``
     this is the query form (attn_quantize_fp8_q): the scale is folded so that
     q_scale * k_scale * softmax_scale * log2(e) is a power of two.
+    With ``hadamard`` the head vectors (last axis) are first rotated by
+    Hadamard blocks (attn_quantize_fp8_hadamard): for Q and K only.
     Returns (codes uint8 tensor shaped like x, scale float32 device tensor [1]).
     """
     _need(x, "x")
@@ -118,7 +123,17 @@ def attn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None, scale: t
     out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
     scale = torch.empty(1, dtype=torch.float32, device=x.device) if scale is None else scale
     _need(out, "out")
-    if k_scale is None:
+    if hadamard:
+        if k_scale is not None:
+            _need(k_scale, "k_scale")
+            if softmax_scale is None:
+                raise ValueError("the folded query scale needs softmax_scale")
+        _check("attn_quantize_fp8_hadamard",
+               lib().attn_quantize_fp8_hadamard(x.data_ptr(), xdt, x.numel(), x.shape[-1], out.data_ptr(),
+                                                scale.data_ptr(), _ptr(k_scale),
+                                                float(softmax_scale) if softmax_scale is not None else 0.0,
+                                                _stream(stream)))
+    elif k_scale is None:
         _check("attn_quantize_fp8",
                lib().attn_quantize_fp8(x.data_ptr(), xdt, x.numel(), out.data_ptr(), scale.data_ptr(),
                                        _stream(stream)))
@@ -193,19 +208,26 @@ def attn_prefill_fwd(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True
 
 
 def prefill(q32: torch.Tensor, k32: torch.Tensor, v32: torch.Tensor, dtype: str = "fp8", causal=True,
-            stream=None, fold_q: bool = True):
+            stream=None, fold_q: bool = True, hadamard: bool = False):
     """The whole path on float32 device inputs: input step, then attention.
 
     dtype "fp8": per-tensor quantization (scales stay on the device and are
     read by the kernel, so no host synchronisation); with ``fold_q`` the query
-    takes the folded scale (see attn_quantize_fp8). "bf16": RNE cast.
+    takes the folded scale (see attn_quantize_fp8). With ``hadamard`` (fp8
+    only; implies ``fold_q``) Q and K are rotated before the cast.
+    "bf16": RNE cast.
     Returns (o, lse, extras) where extras holds the codes and the scale tensor.
     """
+    if hadamard and dtype != "fp8":
+        raise ValueError("the Hadamard rotation applies to the fp8 path")
     if dtype == "fp8":
         scales = torch.empty(3, dtype=torch.float32, device=q32.device)
-        k8, _ = attn_quantize_fp8(k32, scale=scales[1:2], stream=stream)
+        k8, _ = attn_quantize_fp8(k32, scale=scales[1:2], stream=stream, hadamard=hadamard)
         v8, _ = attn_quantize_fp8(v32, scale=scales[2:3], stream=stream)
-        if fold_q:
+        if hadamard:
+            q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream, k_scale=scales[1:2],
+                                      softmax_scale=1.0 / math.sqrt(q32.shape[-1]), hadamard=True)
+        elif fold_q:
             q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream, k_scale=scales[1:2],
                                       softmax_scale=1.0 / math.sqrt(q32.shape[-1]))
         else:

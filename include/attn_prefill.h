@@ -128,6 +128,31 @@ int attn_quantize_fp8_q(const void* x, int x_dtype, int64_t n, uint8_t* x8, floa
                         const float* d_k_scale, float softmax_scale, hipStream_t stream);
 
 /*
+ * The FP8 input step with a Hadamard rotation of the head vectors, for Q and
+ * K (aicronaca.it, section "Perché l'FP8 non basta da solo": rotating Q and K
+ * before the FP8 cast about halves the input quantization error). V is not
+ * rotated.
+ *   x, x_dtype, n, x8, d_scale   as attn_quantize_fp8; x is rows of d elements.
+ *   d          head dim, the length of the last axis (n % d == 0). Rotation
+ *              blocks of b = largest power of two dividing d, at most 128,
+ *              must be 64 or 128 (d = 128: one block; d = 192: three of 64),
+ *              else ATTN_ERR_UNSUPPORTED.
+ *   d_k_scale  NULL: key tensor. Else query tensor, with d_k_scale and
+ *              softmax_scale as in attn_quantize_fp8_q.
+ * Each b-element block of a row becomes y = x H_b, H_b the unnormalized
+ * Sylvester Hadamard matrix (entry (i,j) = (-1)^popcount(i & j)), formed in
+ * fp64. Then (q H)(k H)^T = b q.k^T. The absmax is the max of fp32(|y|).
+ * The code scale follows the rule of attn_quantize_fp8 (key) or
+ * attn_quantize_fp8_q (query) on that absmax, and
+ * code = e4m3fn(fp32(y * fp64(1/scale))), ties to even. d_scale receives the
+ * code scale for a key and the code scale / b for a query. The dequantized
+ * products are then the unrotated q.k, and the query keeps the folded
+ * property, so the attention call needs no change. Deterministic.
+ */
+int attn_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, int d, uint8_t* x8, float* d_scale,
+                               const float* d_k_scale, float softmax_scale, hipStream_t stream);
+
+/*
  * BF16 input step: float32 -> bfloat16, round to nearest, ties to even.
  *   x  device float32[n];  y  device bfloat16[n] (as uint16 bits);  0 < n < 2^40.
  */

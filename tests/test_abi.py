@@ -23,7 +23,7 @@ FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced by host
 def test_exports_every_header_function():
     names = ops.header_functions()
     assert set(names) == {"attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_quantize_fp8", "attn_quantize_fp8_q",
-                          "attn_cast_bf16", "attn_strerror", "attn_abi_version"}
+                          "attn_quantize_fp8_hadamard", "attn_cast_bf16", "attn_strerror", "attn_abi_version"}
     L = ctypes.CDLL(build_mod.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -95,3 +95,20 @@ def test_quantize_and_cast_reject_bad_arguments():
     assert L.attn_quantize_fp8(FAKE, 0, 16, FAKE + 1024, FAKE + 8, None) == INVALID  # scale aliases x
     assert L.attn_cast_bf16(None, 8, FAKE, None) == INVALID
     assert L.attn_cast_bf16(FAKE, -5, FAKE, None) == INVALID
+
+
+def test_quantize_hadamard_rejects_bad_arguments():
+    f = ops.lib().attn_quantize_fp8_hadamard
+    # x: 256 fp32 at FAKE; codes at FAKE + 4096; scale at FAKE + 8192; key scale at FAKE + 8256
+    x, x8, sc, ks = FAKE, FAKE + 4096, FAKE + 8192, FAKE + 8256
+    assert f(x, 0, 288, 96, x8, sc, None, 0.0, None) == UNSUPPORTED     # 32-wide blocks
+    assert f(x, 0, 256, 32, x8, sc, None, 0.0, None) == UNSUPPORTED
+    assert f(x, 0, 256, 0, x8, sc, None, 0.0, None) == INVALID
+    assert f(x, 0, 200, 128, x8, sc, None, 0.0, None) == INVALID        # n not a multiple of d
+    assert f(x, 0, 0, 128, x8, sc, None, 0.0, None) == INVALID
+    assert f(None, 0, 256, 128, x8, sc, None, 0.0, None) == INVALID
+    assert f(x, 3, 256, 128, x8, sc, None, 0.0, None) == UNSUPPORTED
+    assert f(x, 0, 256, 128, x8, x + 16, None, 0.0, None) == INVALID    # scale inside x
+    assert f(x, 0, 384, 192, x8, sc, ks, 0.0, None) == INVALID          # query: softmax scale 0
+    assert f(x, 0, 384, 192, x8, sc, sc, 0.1, None) == INVALID          # key scale aliases d_scale
+    assert f(x, 0, 384, 192, x8, sc, ks + 2, 0.1, None) == INVALID      # misaligned key scale
