@@ -12,7 +12,7 @@ namespace attn {
 
 // Kernel variants: (dtype, d_qk, d_v) -> tile configuration.
 using CfgF8D128 = FwdCfg<true, 128, 128, 64, 4>;
-using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4>;
+using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4, false>;  // the NSTAGE-unrolled loop spills here
 using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4>;
 using CfgBFD192 = FwdCfg<false, 192, 128, 32, 4>;
 

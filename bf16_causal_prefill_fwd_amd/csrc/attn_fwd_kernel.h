@@ -58,7 +58,7 @@ struct FwdParams {
   int xcd_remap;
 };
 
-template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_>
+template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_, bool STAGE_UNROLL_ = true>
 struct FwdCfg {
   static constexpr bool FP8 = FP8_;
   static constexpr int DQK = DQK_, DV = DV_, BN = BN_;
@@ -76,6 +76,11 @@ struct FwdCfg {
   static constexpr int KTILE = BN * KROW;
   static constexpr int VTILE = BN * VROW;
   static constexpr int NSTAGE = NSTAGE_;             // K ring and V ring depth
+  // main loop unrolled by NSTAGE (every ring stage a constant LDS offset, no
+  // per-step address arithmetic) rather than by 2 (the score parity only);
+  // the longer loop body needs more registers, so a configuration that
+  // would spill keeps the short one
+  static constexpr bool STAGE_UNROLL = STAGE_UNROLL_;
   static constexpr int LOOKAHEAD = FP8 ? 2 : 1;      // MFMA jobs whose LDS operand reads are in flight
   // folded score form available (the scaled MFMA exists for FP8 only)
   static constexpr bool FOLDABLE = FP8;
@@ -94,6 +99,7 @@ struct FwdCfg {
   static_assert(DV % 32 == 0 && DQK % 64 == 0, "head dims");
   static_assert(KTILE % (16 * NTHREADS) == 0 && VTILE % (16 * NTHREADS) == 0, "staging split");
   static_assert(NSTAGE >= 2 && INFLIGHT < 64, "ring depth / vmcnt range");
+  static_assert(!STAGE_UNROLL || NSTAGE % 2 == 0, "the stage index must carry the score parity");
   static_assert(WG_PER_CU * LDS_BYTES <= 160 * 1024, "LDS of the workgroups of one CU");
 };
 
@@ -205,6 +211,17 @@ constexpr float kLazyMaxThreshold = 256.f;
 //    through its E8M0 operand scales and starts its accumulation from -m, so
 //    it hands over t itself and the fma disappears from the softmax. The
 //    input step can pick Q's per-tensor scale so that c is a power of two.
+// f(integral_constant<int, I>) for I = B .. E-1, in order, while it returns true
+template <int B, int E, class F>
+__device__ __forceinline__ bool static_for_steps(F&& f) {
+  if constexpr (B == E) {
+    return true;
+  } else {
+    if (!f(std::integral_constant<int, B>{})) return false;
+    return static_for_steps<B + 1, E>(f);
+  }
+}
+
 enum ScoreForm { kScaleFma = 0, kScaleFolded = 1 };
 
 template <class C, int FORM>
@@ -539,9 +556,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   auto job_at = [](int pos) constexpr -> int {
     return ALTERNATE ? ((pos & 1) ? C::NPV + (pos >> 1) : (pos >> 1)) : pos;
   };
-  // ---- one pipeline step n with parity P (tile n's scores in sbuf[P])
-  auto step = [&](int n, auto Pc) {
-    constexpr int P = decltype(Pc)::value, Q = 1 - P;
+  // ---- one pipeline step n. M: n % NS when the loop is unrolled by NS
+  // (then every LDS stage address is a constant offset), else n % 2 (M = -1,
+  // stage addresses computed). The parity P = n & 1 says where tile n's
+  // scores are (sbuf[P]). FIRST: n == 0.
+  auto step = [&](int n, auto Mc, auto FIRSTc) {
+    constexpr int M = decltype(Mc)::value;
+    constexpr bool FIRST = decltype(FIRSTc)::value;
+    constexpr bool CONST_STAGE = C::STAGE_UNROLL;
+    constexpr int P = M & 1, Q = 1 - P;
+    using Pc = std::integral_constant<int, P>;
     const int n0 = n * BN;
     // mask (wave-uniform branch: tiles that straddle this wave's diagonal,
     // lie wholly past its rows, or cross the sequence end)
@@ -558,8 +582,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       }
     }
     // V(n-1) sits in stage (n-1) % NS; at n = 0 P is zero and stage 0 (V(0)) is read
-    const ATTN_LDS char* vl = v_lds + (n == 0 ? 0 : (n - 1) % NS) * C::VTILE;
-    const ATTN_LDS char* kl = k_lds + ((n + 1) % NS) * C::KTILE;
+    const int vst = FIRST ? 0 : (CONST_STAGE ? (M + NS - 1) % NS : (n - 1) % NS);
+    const int kst = CONST_STAGE ? (M + 1) % NS : (n + 1) % NS;
+    const ATTN_LDS char* vl = v_lds + vst * C::VTILE;
+    const ATTN_LDS char* kl = k_lds + kst * C::KTILE;
     // MFMA jobs interleaved with the softmax chunks of tile n; job j's LDS
     // reads go out LOOKAHEAD jobs ahead (a ring of LOOKAHEAD + 1 operands)
     float lsum = 0.f;
@@ -586,7 +612,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       // chunks are spread evenly over the jobs (the last one follows the
       // last MFMA; the lazy-max check waits at the barrier anyway)
       const int c_end = (j + 1) * NCHUNK / NJOB;
-      for (; c < c_end; ++c) probs_chunk(c, Pc, m_run, lsum, False_{});
+      for (; c < c_end; ++c) probs_chunk(c, Pc{}, m_run, lsum, False_{});
       // issue order: this job's look-ahead reads, then its MFMA; the softmax
       // instructions are left to the scheduler (pinning them measured slower)
       if constexpr (FOLD) {
@@ -601,8 +627,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     __syncthreads();
     // lazy-max check of tile n after the barrier, by when its row sums are
     // complete (the exact path touches registers only)
-    const bool first = FOLD && n == 0;
-    if (wave_any(first | !(lsum <= kLazyMaxThreshold))) exact_path(Pc, lsum, first);
+    const bool first = FOLD && FIRST;
+    if (wave_any(first | !(lsum <= kLazyMaxThreshold))) exact_path(Pc{}, lsum, first);
     l_run += lsum;
   };
 
@@ -625,10 +651,23 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // loaded meanwhile (their stages were last read in step n-1). At the end
   // each wave waits for all but the last NS-2 steps' loads, so K(n+2) and
   // V(n) are complete at the barrier.
-  for (int n = 0; n < T; n += 2) {
-    step(n, std::integral_constant<int, 0>{});
-    if (n + 1 >= T) break;
-    step(n + 1, std::integral_constant<int, 1>{});
+  step(0, std::integral_constant<int, 0>{}, True_{});
+  if constexpr (C::STAGE_UNROLL) {
+    for (int n = 1; n < T; n += NS) {
+      const bool more = static_for_steps<0, NS>([&](auto Ic) {
+        constexpr int i = decltype(Ic)::value;
+        if (n + i >= T) return false;
+        step(n + i, std::integral_constant<int, (1 + i) % NS>{}, False_{});
+        return true;
+      });
+      if (!more) break;
+    }
+  } else {
+    for (int n = 1; n < T; n += 2) {
+      step(n, std::integral_constant<int, 1>{}, False_{});
+      if (n + 1 >= T) break;
+      step(n + 1, std::integral_constant<int, 0>{}, False_{});
+    }
   }
   // last tile T-1: its lazy-max check, then its P.V (V stage complete: waited
   // at the end of step T-2)
