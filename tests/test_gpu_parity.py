@@ -203,3 +203,51 @@ def test_full_size_sampled_rows(name):
         bad += (o2.view(torch.int16) != o.view(torch.int16)).sum() + (l2 != lse).sum()
     torch.cuda.synchronize()
     assert bad.item() == 0, h0
+
+
+# ---------------------------------------------------------------- tile-boundary sweep and exact-path stress
+
+BOUNDARY_S = [63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 320, 449]
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_sequence_lengths_around_tile_boundaries(dtype):
+    # 64-key steps, 128-row workgroups, a main loop unrolled by the ring depth
+    # (4): these lengths give every tile count mod 4 and every ragged tail
+    worst = (0.0, 0.0)
+    for S in BOUNDARY_S:
+        w = Workload(f"boundary_{S}", 1, S, 4, 2, 128, 128, dtype, "gauss")
+        q, k, v, o, lse, ex = run_case(w, seed=S)
+        ref = prefill_reference(q, k, v, dtype, fold_q=True)
+        err = rel_l2(o.float().cpu().numpy().astype(np.float64), ref["o"])
+        lerr = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref["lse"])))
+        worst = (max(worst[0], err), max(worst[1], lerr))
+        assert err <= O_TOL[dtype] and lerr <= LSE_TOL, (S, err, lerr)
+    print(f"  worst over {len(BOUNDARY_S)} lengths: O rel-L2 {worst[0]:.3e}  LSE max-abs {worst[1]:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_running_max_grows_every_tile(dtype):
+    # scores rise with the key index (k_j = (0.5 + 2j/S) * u, q_i = 4 u for a
+    # random unit-scale u), so each new tile holds the row's largest score
+    # and the exact-maximum path (running-max update, O and l rescale) runs
+    # on nearly every step
+    S, H = 700, 2
+    rng = np.random.default_rng(21)
+    u = rng.standard_normal(128).astype(np.float32)
+    u /= np.float32(np.linalg.norm(u) / np.sqrt(128))
+    ramp = (0.5 + 2.0 * np.arange(S, dtype=np.float32) / S)[None, :, None, None]
+    k = np.ascontiguousarray(np.broadcast_to(ramp * u, (1, S, H, 128))).astype(np.float32)
+    k += 0.05 * rng.standard_normal(k.shape).astype(np.float32)
+    q = np.ascontiguousarray(np.broadcast_to(4.0 * u, (1, S, H, 128))).astype(np.float32)
+    v = rng.standard_normal((1, S, H, 128)).astype(np.float32)
+    print(f"case rising scores {dtype} S={S}", flush=True)
+    o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), dtype)
+    torch.cuda.synchronize()
+    ref = prefill_reference(q, k, v, dtype, fold_q=True)
+    err = rel_l2(o.float().cpu().numpy().astype(np.float64), ref["o"])
+    lerr = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref["lse"])))
+    print(f"  O rel-L2 {err:.3e}  LSE max-abs {lerr:.3e}", flush=True)
+    assert err <= O_TOL[dtype] and lerr <= LSE_TOL
+    o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], d_scales=ex["scales"] if dtype == "fp8" else None)
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(l2, lse)
