@@ -17,7 +17,8 @@
 //    without relying on another wave's phase (the pages overlap the two
 //    with a two-wave ping-pong: ai4bro.com, "How does ZYFA work?";
 //    aicronaca.it, "Perché l'FP8 non basta da solo"). The LDS reads of the
-//    MFMA operands run two MFMAs ahead.
+//    MFMA operands run two MFMAs ahead. The step loop is unrolled by the
+//    ring depth, so every LDS stage address is a constant offset.
 //  * Key/value tiles go from HBM straight into LDS with coalesced 16-byte
 //    global-to-LDS loads, into K and V rings of NSTAGE stages, issued
 //    NSTAGE-1 steps before use; every wave waits only for its own loads
@@ -383,8 +384,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // Scores and P operands are double-buffered by tile parity: step n reads
   // the scores of tile n from sbuf[n&1] and writes tile n+1's into
   // sbuf[~n&1]; it reads the P operand of tile n-1 from pbuf[~n&1] and
-  // writes tile n's into pbuf[n&1]. The loop is unrolled by two so every
-  // index is a constant (no register copies between steps).
+  // writes tile n's into pbuf[n&1]. The loop is unrolled (by the ring depth,
+  // or by two) so every index is a constant (no register copies between
+  // steps).
   f32x16 sbuf[2][C::NST];
   constexpr int PREGS = C::FP8 ? 2 : C::PV_STEPS;   // FP8: 2 x i32x4 per 64 keys; BF16: one bf16x8 per 16 keys
   typedef typename std::conditional<C::FP8, i32x4, bf16x8>::type PVec;
