@@ -45,10 +45,16 @@ KERNEL_SOURCES = ["attn_fwd_kernel.h", "common.h", "api.hip"]
 
 
 def kernel_source_hash() -> str:
+    """Hash of the attention kernel's sources with comments and blank space removed
+    (a comment edit does not invalidate the stored counter readings)."""
+    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bf16_causal_prefill_fwd_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "bf16_causal_prefill_fwd_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
