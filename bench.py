@@ -44,17 +44,21 @@ HEADLINE = "mha_fp8_32k"
 KERNEL_SOURCES = ["attn_fwd_kernel.h", "common.h", "api.hip"]
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without comments, blank space collapsed to single spaces."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     """Hash of the attention kernel's sources with comments and blank space removed
     (a comment edit does not invalidate the stored counter readings)."""
-    import re
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "bf16_causal_prefill_fwd_amd", "csrc", name)) as f:
-            text = f.read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
