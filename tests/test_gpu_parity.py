@@ -65,6 +65,9 @@ SMALL = [
     Workload("noncausal_fp8", 1, 300, 4, 2, 128, 128, "fp8", "gauss", causal=False),
     Workload("noncausal_bf16", 1, 200, 2, 1, 128, 128, "bf16", "gauss", causal=False),
     Workload("noncausal_mla_fp8", 1, 150, 2, 2, 192, 128, "fp8", "mla", causal=False),
+    # 16 query heads per kv head: one XCD unit spans 16 query heads
+    Workload("gqa_group16_fp8", 1, 300, 16, 1, 128, 128, "fp8", "outlier"),
+    Workload("gqa_group8_bf16", 2, 150, 16, 2, 128, 128, "bf16", "gauss"),
 ]
 
 
@@ -251,3 +254,24 @@ def test_running_max_grows_every_tile(dtype):
     assert err <= O_TOL[dtype] and lerr <= LSE_TOL
     o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], d_scales=ex["scales"] if dtype == "fp8" else None)
     assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(l2, lse)
+
+
+def test_long_context_64k_sampled_rows():
+    # twice the pages' longest context: 1,024 key tiles and 512 query tiles per
+    # head, past every 32-bit product of the 32K shape
+    w = Workload("long_64k_fp8", 1, 65536, 8, 8, 128, 128, "fp8", "gauss")
+    q, k, v, o, lse, ex = run_case(w, seed=5)
+    rng = np.random.default_rng(64)
+    rows = [(0, int(h), int(i)) for h in (0, 7) for i in sorted(set([0, 1, 32767, 32768, 65534, 65535]
+                                                                     + list(rng.integers(0, w.S, 4))))]
+    ref = prefill_reference(q, k, v, "fp8", rows=rows, fold_q=True)
+    sc = ex["scales"].cpu().numpy()
+    assert np.array_equal(sc, np.float32([ref["q_scale"], ref["k_scale"], ref["v_scale"]]))
+    bi = torch.tensor([r[0] for r in rows]); hi = torch.tensor([r[1] for r in rows])
+    ii = torch.tensor([r[2] for r in rows])
+    og = o[bi, ii, hi].float().cpu().numpy().astype(np.float64)
+    lg = lse[bi, hi, ii].cpu().numpy().astype(np.float64)
+    err = rel_l2(og, ref["o_rows"])
+    lerr = float(np.max(np.abs(lg - ref["lse_rows"])))
+    print(f"  {len(rows)} rows: O rel-L2 {err:.3e}  LSE max-abs {lerr:.3e}", flush=True)
+    assert err <= O_TOL["fp8"] and lerr <= LSE_TOL
