@@ -178,33 +178,47 @@ def sustained(seconds: float, attention, flops: float, stream, peak_tflops: floa
     return rec
 
 
-def cpu_baseline(w, q, k, v, n_heads: int = 4) -> dict:
+def cpu_baseline(w, q, k, v, n_heads: int = 4, hadamard: bool = False, o_gpu=None, lse_gpu=None) -> dict:
     """The fp64 oracle on the first query heads of batch 0, every query row.
 
     n_heads whole causal head slices (about 10-15 s of CPU work at the 32K
-    shape on a 16-core host) with the kv heads they read.
+    shape on a 16-core host) with the kv heads they read, quantized as the
+    GPU input step does (with ``hadamard``, Q and K rotated first). Given the
+    GPU's O and LSE for the same slices (numpy, [S, n_heads, d_v] and
+    [n_heads, S]), their errors against this exact result are reported too.
+    Also times the whole tiny configuration (B=1, S=512, H=2) on one thread.
     """
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import causal_attention, dequantize_fp8, encode_with_scale, per_tensor_scale, \
-        per_tensor_scale_folded, bf16_encode, bf16_decode
+        per_tensor_scale_folded, bf16_encode, bf16_decode, prefill_reference
+    from oracle.rotation import hadamard_encode, hadamard_scales
+    from bf16_causal_prefill_fwd_amd.workloads import make_inputs
 
     G = w.Hq // w.Hkv
     nh = min(n_heads, w.Hq)
     nkv = max(1, nh // G)
+    sm = 1.0 / math.sqrt(w.d_qk)
     t0 = time.perf_counter()
-    cuts = ((q, nh), (k, nkv), (v, nkv))
-    if w.dtype == "fp8":
+    if w.dtype == "fp8" and hadamard:
+        kcs, ks = hadamard_scales(k)
+        qcs, qs = hadamard_scales(q, k_scale=ks, softmax_scale=sm)
+        vs = per_tensor_scale(v)
+        sl = [dequantize_fp8(hadamard_encode(q[:1, :, 0:nh], qcs), qs),
+              dequantize_fp8(hadamard_encode(k[:1, :, 0:nkv], kcs), ks),
+              dequantize_fp8(encode_with_scale(v[:1, :, 0:nkv], vs), vs)]
+    elif w.dtype == "fp8":
         ks, vs = per_tensor_scale(k), per_tensor_scale(v)
-        scales = [per_tensor_scale_folded(q, ks, 1.0 / math.sqrt(w.d_qk)), ks, vs]
+        scales = [per_tensor_scale_folded(q, ks, sm), ks, vs]
+        cuts = ((q, nh), (k, nkv), (v, nkv))
         sl = [dequantize_fp8(encode_with_scale(x[:1, :, 0:n], s), s) for (x, n), s in zip(cuts, scales)]
     else:
-        sl = [bf16_decode(bf16_encode(x[:1, :, 0:n])) for x, n in cuts]
-    causal_attention(*sl, causal=w.causal)
+        sl = [bf16_decode(bf16_encode(x[:1, :, 0:n])) for x, n in ((q, nh), (k, nkv), (v, nkv))]
+    O, L = causal_attention(*sl, causal=w.causal)
     dt = time.perf_counter() - t0
     flops = nh * (float(w.S) ** 2 * (w.d_qk + w.d_v) if w.causal else 2.0 * float(w.S) ** 2 * (w.d_qk + w.d_v))
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    return {
+    rec = {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
@@ -213,6 +227,24 @@ def cpu_baseline(w, q, k, v, n_heads: int = 4) -> dict:
                    f"(kv heads 0-{nkv - 1}, G={G}), all {w.S} rows: {nh}/{w.B * w.Hq} of the workload, "
                    f"{flops / 1e9:.1f} GFLOP in {dt:.2f} s; host os.cpu_count()={os.cpu_count()}"),
     }
+    if o_gpu is not None and lse_gpu is not None:
+        import numpy as np
+        og = np.asarray(o_gpu, dtype=np.float64)
+        rec["gpu_error_on_sample"] = {
+            "o_rel_l2": float(np.linalg.norm(og - O[0]) / np.linalg.norm(O[0])),
+            "lse_max_abs": float(np.max(np.abs(np.asarray(lse_gpu, dtype=np.float64) - L[0]))),
+            "bars": {"o_rel_l2": 3e-2 if w.dtype == "fp8" else 5e-3, "lse_max_abs": 1e-2},
+        }
+    # the tiny configuration in full, one BLAS thread
+    tq, tk, tv = make_inputs("tiny_mha_fp8", seed=0)
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        prefill_reference(tq, tk, tv, "fp8", fold_q=True)
+        t1 = time.perf_counter() - t1
+    tiny_flops = 2 * 512 ** 2 * 256
+    rec["tiny_one_thread"] = {"workload": "tiny_mha_fp8 (B=1, S=512, H=2, d=128, FP8)", "seconds": round(t1, 3),
+                              "gflops": round(tiny_flops / t1 / 1e9, 2), "threads": 1}
+    return rec
 
 
 def main(argv=None) -> int:
@@ -388,7 +420,10 @@ def main(argv=None) -> int:
         rec["sustained"] = None
     if not args.no_cpu_baseline:
         print("# cpu baseline (fp64 oracle, four head slices)", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
+        nh = min(4, w.Hq)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, n_heads=nh, hadamard=args.hadamard,
+                                           o_gpu=o[0, :, 0:nh].float().cpu().numpy(),
+                                           lse_gpu=lse[0, 0:nh].cpu().numpy())
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

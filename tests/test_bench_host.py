@@ -53,9 +53,19 @@ def test_traffic_reading_needs_the_current_sources():
     assert bench.traffic_from_profile("no_such_workload", h) is None
 
 
-def test_cpu_baseline_leg_on_the_tiny_workload():
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_cpu_baseline_leg_on_the_tiny_workload(hadamard):
     w = WORKLOADS["tiny_mha_fp8"]
     q, k, v = make_inputs(w, seed=0)
-    r = bench.cpu_baseline(w, q, k, v)
+    from oracle import prefill_reference
+    ref = prefill_reference(q, k, v, "fp8", fold_q=True, hadamard=hadamard)
+    # stand-ins for the GPU's outputs: the exact result, and one perturbed by 1 %
+    r = bench.cpu_baseline(w, q, k, v, hadamard=hadamard, o_gpu=ref["o"][0], lse_gpu=ref["lse"][0])
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0 and r["cores"] >= 1
     assert "query heads 0-1" in r["sample"] and "2/2 of the workload" in r["sample"]
+    e = r["gpu_error_on_sample"]
+    assert e["o_rel_l2"] < 1e-12 and e["lse_max_abs"] < 1e-12
+    r = bench.cpu_baseline(w, q, k, v, hadamard=hadamard, o_gpu=ref["o"][0] * 1.01, lse_gpu=ref["lse"][0] + 0.002)
+    assert abs(r["gpu_error_on_sample"]["o_rel_l2"] - 0.01) < 1e-9
+    assert abs(r["gpu_error_on_sample"]["lse_max_abs"] - 0.002) < 1e-9
+    assert r["tiny_one_thread"]["threads"] == 1 and r["tiny_one_thread"]["gflops"] > 0
