@@ -54,5 +54,26 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     return out
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_abi", "abi_caller.cpp")
+C_CALLER = os.path.join(ROOT, "tests", "c_abi", "abi_caller")
+
+
+def build_c_caller(verbose: bool = False) -> str:
+    """Compile the plain C++ ABI caller used by the tests (host code only),
+    linked against the in-tree library; returns its path."""
+    tmp = C_CALLER + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-O2", "-std=c++17", "-Wno-unused-command-line-argument", "-I", INCLUDE, C_CALLER_SRC,
+           "-L", PKG, "-lattn_prefill", "-Wl,-rpath,$ORIGIN/../../bf16_causal_prefill_fwd_amd", "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building the ABI caller")
+    os.replace(tmp, C_CALLER)
+    return C_CALLER
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_caller(verbose=True))
