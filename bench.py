@@ -41,7 +41,7 @@ PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
 HBM_GBS = 8000.0
 METRIC = "causal prefill attention TFLOP/s (FP8, d=128, S=32K) and % of dense FP8 MFMA peak"
 HEADLINE = "mha_fp8_32k"
-KERNEL_SOURCES = ["attn_fwd_kernel.h", "common.h", "api.hip"]
+KERNEL_SOURCES = ["attn_fwd_kernel.h", "common.h", "attn_fwd_launch.h"]
 
 
 def code_only(text: str) -> str:
@@ -311,7 +311,9 @@ def main(argv=None) -> int:
         return 2
 
     def input_step():
-        if w.dtype == "fp8":
+        if w.dtype == "fp8" and not args.hadamard:
+            ops.attn_quantize_fp8_qkv(q32, k32, v32, sm_scale, out=codes, scales=scales, stream=stream)
+        elif w.dtype == "fp8":
             # K and V first: the query's folded scale is derived from K's
             for i in (1, 2):
                 ops.attn_quantize_fp8((q32, k32, v32)[i], out=codes[i], scale=scales[i:i + 1], stream=stream,

@@ -5,17 +5,10 @@
 #include <string.h>
 
 #include "attn_prefill.h"
-#include "attn_fwd_kernel.h"
+#include "attn_fwd_launch.h"
 #include "quantize.h"
 
 namespace attn {
-
-// Kernel variants: (dtype, d_qk, d_v) -> tile configuration.
-using CfgF8D128 = FwdCfg<true, 128, 128, 64, 4>;
-using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4, false>;  // the NSTAGE-unrolled loop spills here
-using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4>;
-using CfgBFD192 = FwdCfg<false, 192, 128, 32, 4>;
-
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -44,16 +37,6 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
-template <class C>
-int launch_fwd(FwdParams prm, hipStream_t stream) {
-  prm.n_mtiles = (prm.S + C::BM - 1) / C::BM;
-  const int64_t units = (int64_t)prm.B * prm.Hkv;
-  const int64_t items = (int64_t)prm.B * prm.Hq * prm.n_mtiles;
-  if (items > 0x7FFFFFFF) return ATTN_ERR_INVALID;
-  prm.xcd_remap = (units % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(attn_fwd_kernel<C>, dim3((unsigned)items), dim3(C::NTHREADS), 0, stream, prm);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
-}
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale, float k_scale,
              float v_scale, const float* d_scales, float softmax_scale, int B, int S, int Hq, int Hkv, int d_qk,
@@ -96,9 +79,11 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, f
   prm.Hkv = Hkv;
   prm.causal = causal;
 
-  if (dtype == ATTN_DTYPE_FP8_E4M3)
-    return d_qk == 128 ? launch_fwd<CfgF8D128>(prm, stream) : launch_fwd<CfgF8D192>(prm, stream);
-  return d_qk == 128 ? launch_fwd<CfgBFD128>(prm, stream) : launch_fwd<CfgBFD192>(prm, stream);
+  switch (launch_attn_fwd(prm, dtype == ATTN_DTYPE_FP8_E4M3, d_qk, stream)) {
+    case kLaunched: return ATTN_OK;
+    case kTooManyWorkgroups: return ATTN_ERR_INVALID;
+    default: return ATTN_ERR_HIP;
+  }
 }
 
 }  // namespace
@@ -160,6 +145,32 @@ int attn_quantize_fp8_q(const void* x, int x_dtype, int64_t n, uint8_t* x8, floa
                         float softmax_scale, hipStream_t stream) {
   if (!d_k_scale) return ATTN_ERR_INVALID;
   return quantize_impl(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, 0, stream);
+}
+
+int attn_quantize_fp8_qkv(const void* q, const void* k, const void* v, int x_dtype, int64_t nq, int64_t nk,
+                          int64_t nv, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* d_scales, float softmax_scale,
+                          hipStream_t stream) {
+  const void* x[3] = {q, k, v};
+  const int64_t n[3] = {nq, nk, nv};
+  uint8_t* const x8[3] = {q8, k8, v8};
+  if (!d_scales || ((uintptr_t)d_scales & 3u)) return ATTN_ERR_INVALID;
+  if (!(isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_ERR_INVALID;
+  if (x_dtype != 0 && x_dtype != 1) return ATTN_ERR_UNSUPPORTED;
+  const char* sb = (const char*)d_scales;
+  for (int i = 0; i < 3; ++i) {
+    if (!x[i] || !x8[i]) return ATTN_ERR_INVALID;
+    if (n[i] <= 0 || n[i] >= ((int64_t)1 << 40)) return ATTN_ERR_INVALID;
+    if (((uintptr_t)x[i] & 15u) || ((uintptr_t)x8[i] & 15u)) return ATTN_ERR_INVALID;
+    const char* xb = (const char*)x[i];
+    const char* xe = xb + n[i] * (x_dtype == 0 ? 4 : 2);
+    const char* ob = (const char*)x8[i];
+    if ((sb + 12 > xb && sb < xe) || (sb + 12 > ob && sb < ob + n[i])) return ATTN_ERR_INVALID;
+  }
+  const int ready = attn::device_ready();
+  if (ready != ATTN_OK) return ready;
+  return attn::launch_quantize_fp8_qkv(x, x_dtype, n, x8, d_scales, softmax_scale, stream) == hipSuccess
+             ? ATTN_OK
+             : ATTN_ERR_HIP;
 }
 
 int attn_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, int d, uint8_t* x8, float* d_scale,

@@ -60,13 +60,15 @@ __device__ __forceinline__ float absmax16(const uint4& w) {
   return m;
 }
 
+// Absmax of x over the workgroups blk = 0 .. nblk-1 assigned to it; folded
+// into *amax_bits.
 template <int XDT>
-__global__ __launch_bounds__(QTHREADS) void amax_kernel(const void* __restrict__ x, int64_t n,
-                                                         uint32_t* amax_bits) {
+__device__ __forceinline__ void amax_body(const void* __restrict__ x, int64_t n, uint32_t* amax_bits, int blk,
+                                          int nblk) {
   constexpr int N = In16<XDT>::N, U = kVecsInFlight;
   float m = 0.f;
-  const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
-  const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
+  const int64_t nthreads = (int64_t)nblk * QTHREADS;
+  const int64_t gtid = (int64_t)blk * QTHREADS + threadIdx.x;
   const int64_t nv = n / N;
   const uint4* xv = (const uint4*)x;
   const int64_t ntrips = nv / U;
@@ -91,6 +93,12 @@ __global__ __launch_bounds__(QTHREADS) void amax_kernel(const void* __restrict__
     for (int w = 1; w < QTHREADS / 64; ++w) r = fmaxf(r, red[w]);
     atomicMax(amax_bits, __float_as_uint(r));
   }
+}
+
+template <int XDT>
+__global__ __launch_bounds__(QTHREADS) void amax_kernel(const void* __restrict__ x, int64_t n,
+                                                         uint32_t* amax_bits) {
+  amax_body<XDT>(x, n, amax_bits, blockIdx.x, gridDim.x);
 }
 
 __device__ __forceinline__ float scale_from_amax(uint32_t bits) {
@@ -120,15 +128,13 @@ __device__ __forceinline__ float quant_scale(uint32_t bits, const float* d_k_sca
   return d_k_scale ? folded_scale_from_amax(bits, *d_k_scale, sm_scale) : scale_from_amax(bits);
 }
 
+// Codes of x with `scale` over the workgroups blk = 0 .. nblk-1 assigned to it.
 template <int XDT>
-__global__ __launch_bounds__(QTHREADS) void quant_kernel(const void* __restrict__ x, int64_t n,
-                                                          const uint32_t* __restrict__ amax_bits,
-                                                          const float* __restrict__ d_k_scale, float sm_scale,
-                                                          uint8_t* __restrict__ out) {
-  const float scale = quant_scale(*amax_bits, d_k_scale, sm_scale);
+__device__ __forceinline__ void quant_body(const void* __restrict__ x, int64_t n, float scale,
+                                           uint8_t* __restrict__ out, int blk, int nblk) {
   constexpr int N = In16<XDT>::N, U = kVecsInFlight;
-  const int64_t nthreads = (int64_t)gridDim.x * QTHREADS;
-  const int64_t gtid = (int64_t)blockIdx.x * QTHREADS + threadIdx.x;
+  const int64_t nthreads = (int64_t)nblk * QTHREADS;
+  const int64_t gtid = (int64_t)blk * QTHREADS + threadIdx.x;
   const int64_t nv = n / N;
   const uint4* xv = (const uint4*)x;
   // N codes of one vector: 4 bytes (fp32 input) or 8 bytes (bf16 input)
@@ -157,6 +163,59 @@ __global__ __launch_bounds__(QTHREADS) void quant_kernel(const void* __restrict_
   for (int64_t i = ntrips * U + gtid; i < nv; i += nthreads) encode(xv[i], i);
   for (int64_t e = nv * N + gtid; e < n; e += nthreads)
     out[e] = (uint8_t)(cvt_fp8x2(__fdiv_rn(In16<XDT>::load1(x, e), scale), 0.f, 0, false) & 0xFF);
+}
+
+template <int XDT>
+__global__ __launch_bounds__(QTHREADS) void quant_kernel(const void* __restrict__ x, int64_t n,
+                                                          const uint32_t* __restrict__ amax_bits,
+                                                          const float* __restrict__ d_k_scale, float sm_scale,
+                                                          uint8_t* __restrict__ out) {
+  quant_body<XDT>(x, n, quant_scale(*amax_bits, d_k_scale, sm_scale), out, blockIdx.x, gridDim.x);
+}
+
+// ---- Q, K and V in one pass each: the workgroups of one launch are split
+// into three ranges, one per tensor (0 = Q, 1 = K, 2 = V). The absmax of Q
+// does not depend on K, and Q's folded scale needs only K's absmax, so one
+// absmax launch and one encode launch serve all three tensors; the codes and
+// scales are those of three separate calls (K, V plain, Q folded).
+struct Qkv3 {
+  const void* x[3];
+  int64_t n[3];
+  uint8_t* out[3];
+  int first[3];  // first workgroup of each range
+  int nblk[3];
+  uint32_t* bits;  // device float[3]: absmax bits, then the scales {q, k, v}
+  float sm_scale;
+};
+
+__device__ __forceinline__ int qkv_range(const Qkv3& a, int bid) {
+  return bid >= a.first[2] ? 2 : (bid >= a.first[1] ? 1 : 0);
+}
+
+__global__ void amax3_reset_kernel(uint32_t* bits) {
+  if (threadIdx.x < 3) bits[threadIdx.x] = 0u;
+}
+
+template <int XDT>
+__global__ __launch_bounds__(QTHREADS) void amax3_kernel(Qkv3 a) {
+  const int i = qkv_range(a, blockIdx.x);
+  amax_body<XDT>(a.x[i], a.n[i], a.bits + i, blockIdx.x - a.first[i], a.nblk[i]);
+}
+
+template <int XDT>
+__global__ __launch_bounds__(QTHREADS) void quant3_kernel(Qkv3 a) {
+  const int i = qkv_range(a, blockIdx.x);
+  const float scale = i == 0 ? folded_scale_from_amax(a.bits[0], scale_from_amax(a.bits[1]), a.sm_scale)
+                             : scale_from_amax(a.bits[i]);
+  quant_body<XDT>(a.x[i], a.n[i], scale, a.out[i], blockIdx.x - a.first[i], a.nblk[i]);
+}
+
+__global__ void scale3_finalize_kernel(uint32_t* bits, float sm_scale) {
+  const float ks = scale_from_amax(bits[1]), vs = scale_from_amax(bits[2]);
+  const float qs = folded_scale_from_amax(bits[0], ks, sm_scale);
+  bits[0] = __float_as_uint(qs);
+  bits[1] = __float_as_uint(ks);
+  bits[2] = __float_as_uint(vs);
 }
 
 // Replaces the absmax bits by the stored scale: the scale the codes were
@@ -391,6 +450,32 @@ hipError_t launch_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, i
   }
   const float post = d_k_scale ? 1.0f / (float)block : 1.0f;
   hipLaunchKernelGGL(scale_finalize_kernel, dim3(1), dim3(1), 0, stream, bits, d_k_scale, sm_scale, post);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8_qkv(const void* const x[3], int x_dtype, const int64_t n[3], uint8_t* const x8[3],
+                                   float* d_scales, float sm_scale, hipStream_t stream) {
+  Qkv3 a{};
+  int total = 0;
+  for (int i = 0; i < 3; ++i) {
+    a.x[i] = x[i];
+    a.n[i] = n[i];
+    a.out[i] = x8[i];
+    a.first[i] = total;
+    a.nblk[i] = stream_grid(n[i]);
+    total += a.nblk[i];
+  }
+  a.bits = (uint32_t*)d_scales;
+  a.sm_scale = sm_scale;
+  hipLaunchKernelGGL(amax3_reset_kernel, dim3(1), dim3(64), 0, stream, a.bits);
+  if (x_dtype == 0) {
+    hipLaunchKernelGGL(amax3_kernel<0>, dim3(total), dim3(QTHREADS), 0, stream, a);
+    hipLaunchKernelGGL(quant3_kernel<0>, dim3(total), dim3(QTHREADS), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(amax3_kernel<1>, dim3(total), dim3(QTHREADS), 0, stream, a);
+    hipLaunchKernelGGL(quant3_kernel<1>, dim3(total), dim3(QTHREADS), 0, stream, a);
+  }
+  hipLaunchKernelGGL(scale3_finalize_kernel, dim3(1), dim3(1), 0, stream, a.bits, sm_scale);
   return hipGetLastError();
 }
 

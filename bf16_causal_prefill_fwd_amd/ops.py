@@ -42,6 +42,8 @@ _SIGNATURES = {
                                      _c_void_p]),
     "attn_quantize_fp8_hadamard": (_c_int, [_c_void_p, _c_int, _c_int64, _c_int, _c_void_p, _c_void_p, _c_void_p,
                                             _c_float, _c_void_p]),
+    "attn_quantize_fp8_qkv": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int64, _c_int64, _c_int64,
+                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float, _c_void_p]),
     "attn_cast_bf16": (_c_int, [_c_void_p, _c_int64, _c_void_p, _c_void_p]),
     "attn_strerror": (ctypes.c_char_p, [_c_int]),
     "attn_abi_version": (_c_int, []),
@@ -147,6 +149,33 @@ def attn_quantize_fp8(x: torch.Tensor, out: torch.Tensor | None = None, scale: t
     return out, scale
 
 
+def attn_quantize_fp8_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float,
+                          out=None, scales: torch.Tensor | None = None, stream=None):
+    """The FP8 input step of one attention call in one pass per kind of work
+    (attn_quantize_fp8_qkv): K and V with plain scales, Q with the folded one.
+    Returns ((q8, k8, v8) uint8 tensors shaped like the inputs, scales float32
+    device tensor [3] = {q_scale, k_scale, v_scale})."""
+    xs = (q, k, v)
+    dts = {t.dtype for t in xs}
+    if dts == {torch.float32}:
+        xdt = 0
+    elif dts == {torch.bfloat16}:
+        xdt = 1
+    else:
+        raise ValueError("q, k, v must all be float32 or all bfloat16")
+    for name, t in zip("qkv", xs):
+        _need(t, name)
+    out = tuple(torch.empty(t.shape, dtype=torch.uint8, device=t.device) for t in xs) if out is None else out
+    scales = torch.empty(3, dtype=torch.float32, device=q.device) if scales is None else scales
+    for t in (*out, scales):
+        _need(t, "output")
+    _check("attn_quantize_fp8_qkv",
+           lib().attn_quantize_fp8_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), xdt, q.numel(), k.numel(),
+                                       v.numel(), out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+                                       scales.data_ptr(), float(softmax_scale), _stream(stream)))
+    return out, scales
+
+
 def attn_cast_bf16(x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """float32 -> bfloat16 (round to nearest even) on the device."""
     _need(x, "x")
@@ -220,6 +249,10 @@ def prefill(q32: torch.Tensor, k32: torch.Tensor, v32: torch.Tensor, dtype: str 
     """
     if hadamard and dtype != "fp8":
         raise ValueError("the Hadamard rotation applies to the fp8 path")
+    if dtype == "fp8" and fold_q and not hadamard:
+        (q8, k8, v8), scales = attn_quantize_fp8_qkv(q32, k32, v32, 1.0 / math.sqrt(q32.shape[-1]), stream=stream)
+        o, lse = attn_prefill_fwd(q8, k8, v8, causal=causal, d_scales=scales, stream=stream)
+        return o, lse, dict(q=q8, k=k8, v=v8, scales=scales)
     if dtype == "fp8":
         scales = torch.empty(3, dtype=torch.float32, device=q32.device)
         k8, _ = attn_quantize_fp8(k32, scale=scales[1:2], stream=stream, hadamard=hadamard)

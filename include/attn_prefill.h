@@ -128,6 +128,24 @@ int attn_quantize_fp8_q(const void* x, int x_dtype, int64_t n, uint8_t* x8, floa
                         const float* d_k_scale, float softmax_scale, hipStream_t stream);
 
 /*
+ * The whole FP8 input step for one attention call: K and V as
+ * attn_quantize_fp8, then Q as attn_quantize_fp8_q with K's scale, in one
+ * absmax launch and one encode launch over the three tensors (fewer, larger
+ * launches than three separate calls; the codes and scales are identical).
+ *   q, k, v      device inputs of nq, nk, nv elements (float32 if x_dtype 0,
+ *                bfloat16 if 1), each 16-byte aligned; 0 < n < 2^40.
+ *   q8, k8, v8   device outputs, e4m3fn codes in the layouts of the inputs.
+ *   d_scales     device float[3] receiving {q_scale (folded), k_scale,
+ *                v_scale}: the d_scales argument of attn_prefill_fwd_ex. Also
+ *                the absmax accumulators while the call's kernels run, so it
+ *                must not overlap any input or output.
+ *   softmax_scale  the attention call's softmax scale (> 0, finite).
+ */
+int attn_quantize_fp8_qkv(const void* q, const void* k, const void* v, int x_dtype, int64_t nq, int64_t nk,
+                          int64_t nv, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* d_scales, float softmax_scale,
+                          hipStream_t stream);
+
+/*
  * The FP8 input step with a Hadamard rotation of the head vectors, for Q and
  * K (aicronaca.it, section "Perché l'FP8 non basta da solo": rotating Q and K
  * before the FP8 cast about halves the input quantization error). V is not

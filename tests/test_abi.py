@@ -23,7 +23,8 @@ FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced by host
 def test_exports_every_header_function():
     names = ops.header_functions()
     assert set(names) == {"attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_quantize_fp8", "attn_quantize_fp8_q",
-                          "attn_quantize_fp8_hadamard", "attn_cast_bf16", "attn_strerror", "attn_abi_version"}
+                          "attn_quantize_fp8_hadamard", "attn_quantize_fp8_qkv", "attn_cast_bf16", "attn_strerror",
+                          "attn_abi_version"}
     L = ctypes.CDLL(build_mod.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -112,3 +113,31 @@ def test_quantize_hadamard_rejects_bad_arguments():
     assert f(x, 0, 384, 192, x8, sc, ks, 0.0, None) == INVALID          # query: softmax scale 0
     assert f(x, 0, 384, 192, x8, sc, sc, 0.1, None) == INVALID          # key scale aliases d_scale
     assert f(x, 0, 384, 192, x8, sc, ks + 2, 0.1, None) == INVALID      # misaligned key scale
+
+
+def test_quantize_qkv_rejects_bad_arguments():
+    f = ops.lib().attn_quantize_fp8_qkv
+    # q, k, v: 256 fp32 each; codes after them; scales (3 floats) at sc
+    q, k, v = FAKE, FAKE + 1024, FAKE + 2048
+    q8, k8, v8, sc = FAKE + 4096, FAKE + 4352, FAKE + 4608, FAKE + 8192
+    ok = (q, k, v, 0, 256, 256, 256, q8, k8, v8, sc, 0.1, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["q", "k", "v", "xdt", "nq", "nk", "nv", "q8", "k8", "v8", "sc", "sm", "st"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+    assert call(q=None) == INVALID
+    assert call(v8=None) == INVALID
+    assert call(sc=None) == INVALID
+    assert call(nk=0) == INVALID
+    assert call(nv=1 << 40) == INVALID
+    assert call(sm=0.0) == INVALID
+    assert call(sm=float("nan")) == INVALID
+    assert call(xdt=2) == UNSUPPORTED
+    assert call(k=k + 8) == INVALID            # misaligned input
+    assert call(q8=q8 + 4) == INVALID          # misaligned codes
+    assert call(sc=sc + 2) == INVALID          # misaligned scales
+    assert call(sc=v + 1020) == INVALID        # scales overlap the end of v
+    assert call(sc=k8 + 16) == INVALID         # scales inside k's codes

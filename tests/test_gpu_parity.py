@@ -275,3 +275,29 @@ def test_long_context_64k_sampled_rows():
     lerr = float(np.max(np.abs(lg - ref["lse_rows"])))
     print(f"  {len(rows)} rows: O rel-L2 {err:.3e}  LSE max-abs {lerr:.3e}", flush=True)
     assert err <= O_TOL["fp8"] and lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("xdt", [torch.float32, torch.bfloat16])
+def test_fused_input_step_matches_separate_calls(xdt):
+    # one absmax and one encode launch over Q, K, V give the codes and scales
+    # of three separate calls (K, V plain; Q folded with K's scale); MLA-like
+    # shapes (K and V of different sizes), lengths that are not a multiple of
+    # the 16-byte vector, an all-zero Q, and a one-element V
+    rng = np.random.default_rng(31)
+    cases = [((1, 333, 4, 192), (1, 333, 4, 192), (1, 333, 4, 128)),
+             ((1, 1000 * 37 + 5,), (2, 3, 1, 7), (1, 1, 1, 1)),
+             ((1, 65, 8, 128), (1, 65, 2, 128), (1, 65, 2, 128))]
+    for n, (sq, sk, sv) in enumerate(cases):
+        xs = [torch.from_numpy((rng.standard_normal(sh) * (1 + 3 * i)).astype(np.float32)).to("cuda").to(xdt)
+              for i, sh in enumerate((sq, sk, sv))]
+        if n == 2:
+            xs[0].zero_()
+        print(f"case fused input step {xdt} shapes {sq} {sk} {sv}", flush=True)
+        sm = 1.0 / math.sqrt(sq[-1])
+        (q8, k8, v8), sc = ops.attn_quantize_fp8_qkv(*xs, sm)
+        k8s, ks = ops.attn_quantize_fp8(xs[1])
+        v8s, vs = ops.attn_quantize_fp8(xs[2])
+        q8s, qs = ops.attn_quantize_fp8(xs[0], k_scale=ks, softmax_scale=sm)
+        torch.cuda.synchronize()
+        assert torch.equal(q8, q8s) and torch.equal(k8, k8s) and torch.equal(v8, v8s)
+        assert torch.equal(sc, torch.cat([qs, ks, vs]))
