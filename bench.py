@@ -256,6 +256,9 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--hadamard", action="store_true",
                     help="FP8: rotate Q and K by Hadamard blocks in the input step (attn_quantize_fp8_hadamard)")
+    ap.add_argument("--seq-len", type=int, default=None, help="override the workload's sequence length")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="override the head count: Hq = Hkv = HEADS (multi-head attention)")
     ap.add_argument("--dist", choices=("gauss", "outlier", "outlier_shared", "mla"), default=None,
                     help="override the workload's input distribution (same shape), e.g. to compare the "
                          "clock and energy of Gaussian and heavy-tailed inputs")
@@ -285,9 +288,19 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU (none visible)", file=sys.stderr)
         return 2
     w = WORKLOADS[args.workload]
-    default_dist = w.dist
+    base = w
     if args.dist is not None:
         w = dataclasses.replace(w, dist=args.dist)
+    if args.seq_len is not None:
+        if args.seq_len < 1:
+            print("--seq-len must be >= 1", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, S=args.seq_len)
+    if args.heads is not None:
+        if args.heads < 1:
+            print("--heads must be >= 1", file=sys.stderr)
+            return 2
+        w = dataclasses.replace(w, Hq=args.heads, Hkv=args.heads)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"# workload {w.name}: generating inputs (seed {args.seed})", file=sys.stderr, flush=True)
@@ -374,8 +387,8 @@ def main(argv=None) -> int:
         del src, dst
 
     src_hash = kernel_source_hash()
-    # HBM traffic does not depend on the values, but the profile names its inputs
-    traffic = traffic_from_profile(w.name, src_hash) if w.dist == default_dist else None
+    # the stored counter readings are for the workload as defined (shape and inputs)
+    traffic = traffic_from_profile(w.name, src_hash) if w == base else None
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
