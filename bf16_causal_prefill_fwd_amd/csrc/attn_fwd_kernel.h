@@ -487,7 +487,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     const float p1 = fast_exp2(log2_prob(sc[t][r + 1], m, SHIFTc));
     const float p2 = fast_exp2(log2_prob(sc[t][r + 2], m, SHIFTc));
     const float p3 = fast_exp2(log2_prob(sc[t][r + 3], m, SHIFTc));
-    lsum += (p0 + p1) + (p2 + p3);
+    // (the first chunk starts the sum: adding it to 0 would cost an add)
+    const float s4 = (p0 + p1) + (p2 + p3);
+    lsum = c == 0 ? s4 : lsum + s4;
     if constexpr (C::FP8) {
       // FP8 operand byte j <- score tile j/16, register j%16: chunk c fills
       // dword (c & 3) of pout[t]
@@ -520,7 +522,6 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[t][r], sc[t][r + 1]));
     mx = fmaxf(mx, swap_halves(mx));
-    lsum = 0.f;
     if constexpr (!FOLD) {
       const float m_new = fmaxf(m_run, mx * c_log2);
       const float alpha = fast_exp2(m_run - m_new);
@@ -604,6 +605,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
 #pragma unroll
     for (int j = 0; j < NJOB; ++j) {
       if (j + LA < NJOB) fr[(j + LA) % (LA + 1)] = load_frag(job_at(j + LA), vl, kl);
+      // chunks are spread evenly over the jobs, each ahead of its job's
+      // MFMA: the first one covers the latency of the step's first operand
+      // reads, and the last MFMA runs on while the wave waits at the barrier
+      const int c_end = (j + 1) * NCHUNK / NJOB;
+      for (; c < c_end; ++c) probs_chunk(c, Pc{}, m_run, lsum, False_{});
+      if constexpr (FOLD) sched_fence();
       run_job(job_at(j), fr[j % (LA + 1)], std::integral_constant<int, Q>{}, std::integral_constant<int, Q>{});
       // this step's loads (K(n+NS), V(n+NS-2)) go out behind the first MFMA,
       // so their address arithmetic overlaps the softmax
@@ -611,14 +618,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
         issue_k(n + NS);
         issue_v(n + NS - 2);
       }
-      // chunks are spread evenly over the jobs (the last one follows the
-      // last MFMA; the lazy-max check waits at the barrier anyway)
-      const int c_end = (j + 1) * NCHUNK / NJOB;
-      for (; c < c_end; ++c) probs_chunk(c, Pc{}, m_run, lsum, False_{});
-      // issue order: this job's look-ahead reads, then its MFMA; the softmax
-      // instructions are left to the scheduler (pinning them measured slower)
+      // issue order: this job's look-ahead reads, then its MFMA. Fma form:
+      // the softmax instructions are left to the scheduler (pinning them
+      // measured slower). Folded form: the scaled MFMA is not matched by
+      // scheduling groups, so fences keep each job's chunk ahead of its MFMA
       if constexpr (FOLD) {
-        // the scaled MFMA is not matched by scheduling groups: fence each job
         sched_fence();
       } else {
         if (j + LA < NJOB) sched_group<kSchedDsRead>(frag_reads(job_at(j + LA)));
