@@ -82,7 +82,7 @@ struct FwdCfg {
   // the longer loop body needs more registers, so a configuration that
   // would spill keeps the short one
   static constexpr bool STAGE_UNROLL = STAGE_UNROLL_;
-  static constexpr int LOOKAHEAD = FP8 ? 2 : 1;      // MFMA jobs whose LDS operand reads are in flight
+  static constexpr int LOOKAHEAD = 2;               // MFMA jobs whose LDS operand reads are in flight
   // folded score form available (the scaled MFMA exists for FP8 only)
   static constexpr bool FOLDABLE = FP8;
   static constexpr int LDS_BYTES = NSTAGE * (KTILE + VTILE);
