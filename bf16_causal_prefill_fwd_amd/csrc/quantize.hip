@@ -137,30 +137,37 @@ __device__ __forceinline__ void quant_body(const void* __restrict__ x, int64_t n
   const int64_t gtid = (int64_t)blk * QTHREADS + threadIdx.x;
   const int64_t nv = n / N;
   const uint4* xv = (const uint4*)x;
-  // N codes of one vector: 4 bytes (fp32 input) or 8 bytes (bf16 input)
-  auto encode = [&](const uint4& w, int64_t vi) {
+  // N codes of one vector (4 bytes for fp32 input, 8 for bf16) into c[0 .. N/4)
+  auto encode = [&](const uint4& w, uint32_t* c) {
     float v[N];
     In16<XDT>::unpack(w, v);
 #pragma unroll
     for (int j = 0; j < N; ++j) v[j] = __fdiv_rn(v[j], scale);
-    int c[N / 4];
 #pragma unroll
     for (int q = 0; q < N / 4; ++q) {
       const int lo = cvt_fp8x2(v[4 * q], v[4 * q + 1], 0, false);
-      c[q] = cvt_fp8x2(v[4 * q + 2], v[4 * q + 3], lo, true);
+      c[q] = (uint32_t)cvt_fp8x2(v[4 * q + 2], v[4 * q + 3], lo, true);
     }
-    if constexpr (N == 4) ((uint32_t*)out)[vi] = (uint32_t)c[0];
-    else ((uint2*)out)[vi] = make_uint2((uint32_t)c[0], (uint32_t)c[1]);
   };
   const int64_t ntrips = nv / U;
   for (int64_t t = gtid; t < ntrips; t += nthreads) {
     uint4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = xv[t * U + u];
+    // the trip's U * N codes are contiguous: written with 16-byte stores
+    uint32_t c[U * N / 4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) encode(w[u], t * U + u);
+    for (int u = 0; u < U; ++u) encode(w[u], c + u * (N / 4));
+    uint4* o4 = (uint4*)(out + t * (U * N));
+#pragma unroll
+    for (int i = 0; i < U * N / 16; ++i) o4[i] = make_uint4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
   }
-  for (int64_t i = ntrips * U + gtid; i < nv; i += nthreads) encode(xv[i], i);
+  for (int64_t i = ntrips * U + gtid; i < nv; i += nthreads) {
+    uint32_t c[N / 4];
+    encode(xv[i], c);
+    if constexpr (N == 4) ((uint32_t*)out)[i] = c[0];
+    else ((uint2*)out)[i] = make_uint2(c[0], c[1]);
+  }
   for (int64_t e = nv * N + gtid; e < n; e += nthreads)
     out[e] = (uint8_t)(cvt_fp8x2(__fdiv_rn(In16<XDT>::load1(x, e), scale), 0.f, 0, false) & 0xFF);
 }
