@@ -266,6 +266,13 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // ---- key tiles of the workgroup (every wave runs every step)
   const int n_kv = p.causal ? min(S, m0 + C::BM) : S;
   const int T = (n_kv + BN - 1) / BN;
+  // a tile starting at key n0 needs the mask for this wave when n0 >
+  // mask_after: causal, when it reaches past row r0 (n0 + BN - 1 > r0);
+  // otherwise when it reaches past the sequence end (n0 + BN > S). Under the
+  // causal mask a tile that crosses the sequence end always lies at or past
+  // the first one that reaches past r0 (r0 < S, or the wave's rows are not
+  // written at all).
+  const int mask_after = p.causal ? r0 - BN + 1 : S - BN;
 
   // ---- Q fragment (B operand of S^T = K.Q^T), loaded once per wave
   constexpr int QREGS = C::FP8 ? 8 : 4;  // ints per k-step
@@ -314,27 +321,38 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     const int row = o / C::VROW;
     v_loff[i] = row * v_stride32 + 16 * v_swz<C::VCH>((o % C::VROW) / 16, row);
   }
-  auto issue_tile = [&](const uint8_t* base, int stride, const int* loff, int nloads, int rowbytes, uint32_t dst,
-                        int n) {
+  // Only tiles from T_full on reach past the sequence end and clamp rows.
+  // The scalar work per tile is kept small (it competes with the vector and
+  // matrix instructions for the wave's issue slots): the tile's byte offset
+  // is one 32 x 32 -> 64-bit product (BN * row stride fits 31 bits, checked
+  // on the host), and the ring stage is a compile-time constant in the
+  // unrolled loop, so each load's LDS address is this wave's ring base plus
+  // a constant.
+  const int T_full = S / BN;
+  const int k_tile_bytes = BN * k_stride32, v_tile_bytes = BN * v_stride32;
+  const uint32_t k_lds_w = k_lds_addr + wave * 1024, v_lds_w = v_lds_addr + wave * 1024;
+  auto issue_tile = [&](const uint8_t* base, int tile_bytes, int stride, const int* loff, int nloads, int rowbytes,
+                        uint32_t dst, int n) {
     const int nn = min(n, T - 1);
-    const uint8_t* tb = base + (int64_t)(nn * BN) * stride;
-    if ((nn + 1) * BN <= S) {
+    const uint8_t* tb = base + (int64_t)nn * tile_bytes;
+    if (nn < T_full) {
 #pragma unroll
-      for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst + (i * C::NWAVES + wave) * 1024);
+      for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst + i * C::NWAVES * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < nloads; ++i) {
         const int row = ((i * C::NWAVES + wave) * 1024 + 16 * lane) / rowbytes;
         const int key = min(nn * BN + row, S - 1);
-        global_to_lds_16_async(tb, loff[i] + (key - nn * BN - row) * stride, dst + (i * C::NWAVES + wave) * 1024);
+        global_to_lds_16_async(tb, loff[i] + (key - nn * BN - row) * stride, dst + i * C::NWAVES * 1024);
       }
     }
   };
-  auto issue_k = [&](int n) {
-    issue_tile(kbase, k_stride32, k_loff, C::KLOADS, C::KROW, k_lds_addr + (n % NS) * C::KTILE, n);
+  // tile n into ring stage `stage` (= n % NS)
+  auto issue_k = [&](int n, int stage) {
+    issue_tile(kbase, k_tile_bytes, k_stride32, k_loff, C::KLOADS, C::KROW, k_lds_w + stage * C::KTILE, n);
   };
-  auto issue_v = [&](int n) {
-    issue_tile(vbase, v_stride32, v_loff, C::VLOADS, C::VROW, v_lds_addr + (n % NS) * C::VTILE, n);
+  auto issue_v = [&](int n, int stage) {
+    issue_tile(vbase, v_tile_bytes, v_stride32, v_loff, C::VLOADS, C::VROW, v_lds_w + stage * C::VTILE, n);
   };
 
   // ---- per-lane LDS read offsets within a stage (the swizzle term depends
@@ -572,8 +590,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     const int n0 = n * BN;
     // mask (wave-uniform branch: tiles that straddle this wave's diagonal,
     // lie wholly past its rows, or cross the sequence end)
-    const bool need_mask = p.causal ? (n0 + BN - 1 > r0) : (n0 + BN > S);
-    if (need_mask) {
+    if (n0 > mask_after) {
 #pragma unroll
       for (int t = 0; t < C::NST; ++t) {
 #pragma unroll
@@ -615,8 +632,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       // this step's loads (K(n+NS), V(n+NS-2)) go out behind the first MFMA,
       // so their address arithmetic overlaps the softmax
       if (j == 0) {
-        issue_k(n + NS);
-        issue_v(n + NS - 2);
+        issue_k(n + NS, CONST_STAGE ? M : n % NS);
+        issue_v(n + NS - 2, CONST_STAGE ? (M + NS - 2) % NS : (n + NS - 2) % NS);
       }
       // issue order: this job's look-ahead reads, then its MFMA. Fma form:
       // the softmax instructions are left to the scheduler (pinning them
@@ -641,9 +658,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // ---- prologue: stages of K(0..NS-1) and V(0..NS-3) in flight, then all
   // published; S^T of tile 0 into sbuf[0].
 #pragma unroll
-  for (int n = 0; n < NS; ++n) issue_k(n);
+  for (int n = 0; n < NS; ++n) issue_k(n, n);
 #pragma unroll
-  for (int n = 0; n < NS - 2; ++n) issue_v(n);
+  for (int n = 0; n < NS - 2; ++n) issue_v(n, n);
   wait_vmcnt<0>();
   __syncthreads();
 #pragma unroll
