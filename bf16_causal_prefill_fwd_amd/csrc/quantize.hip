@@ -150,7 +150,10 @@ __device__ __forceinline__ void quant_body(const void* __restrict__ x, int64_t n
     }
   };
   const int64_t ntrips = nv / U;
-  for (int64_t t = gtid; t < ntrips; t += nthreads) {
+  // trips in reverse order: the absmax pass ends on the tensor's tail, part
+  // of which the memory-side cache still holds when this pass starts
+  for (int64_t t0 = gtid; t0 < ntrips; t0 += nthreads) {
+    const int64_t t = ntrips - 1 - t0;
     uint4 w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = xv[t * U + u];
