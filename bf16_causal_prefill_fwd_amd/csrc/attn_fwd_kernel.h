@@ -334,8 +334,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   const int T_full = S / BN;
   const int k_tile_bytes = BN * k_stride32, v_tile_bytes = BN * v_stride32;
   const uint32_t k_lds_w = k_lds_addr + wave * 1024, v_lds_w = v_lds_addr + wave * 1024;
+  // CHECKc false: the caller guarantees n < T_full (no clamping of any kind)
   auto issue_tile = [&](const uint8_t* base, int tile_bytes, int stride, const int* loff, int nloads, int rowbytes,
-                        uint32_t dst, int n) {
+                        uint32_t dst, int n, auto CHECKc) {
+    if constexpr (!decltype(CHECKc)::value) {
+      const uint8_t* tb = base + (int64_t)n * tile_bytes;
+#pragma unroll
+      for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst + i * C::NWAVES * 1024);
+      return;
+    }
     const int nn = min(n, T - 1);
     const uint8_t* tb = base + (int64_t)nn * tile_bytes;
     if (nn < T_full) {
@@ -351,11 +358,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     }
   };
   // tile n into ring stage `stage` (= n % NS)
-  auto issue_k = [&](int n, int stage) {
-    issue_tile(kbase, k_tile_bytes, k_stride32, k_loff, C::KLOADS, C::KROW, k_lds_w + stage * C::KTILE, n);
+  auto issue_k = [&](int n, int stage, auto CHECKc) {
+    issue_tile(kbase, k_tile_bytes, k_stride32, k_loff, C::KLOADS, C::KROW, k_lds_w + stage * C::KTILE, n, CHECKc);
   };
-  auto issue_v = [&](int n, int stage) {
-    issue_tile(vbase, v_tile_bytes, v_stride32, v_loff, C::VLOADS, C::VROW, v_lds_w + stage * C::VTILE, n);
+  auto issue_v = [&](int n, int stage, auto CHECKc) {
+    issue_tile(vbase, v_tile_bytes, v_stride32, v_loff, C::VLOADS, C::VROW, v_lds_w + stage * C::VTILE, n, CHECKc);
   };
 
   // ---- per-lane LDS read offsets within a stage (the swizzle term depends
@@ -594,7 +601,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // (then every LDS stage address is a constant offset), else n % 2 (M = -1,
   // stage addresses computed). The parity P = n & 1 says where tile n's
   // scores are (sbuf[P]). FIRST: n == 0.
-  auto step = [&](int n, auto Mc, auto FIRSTc) {
+  auto step = [&](int n, auto Mc, auto FIRSTc, auto CHECKc) {
     constexpr int M = decltype(Mc)::value;
     constexpr bool FIRST = decltype(FIRSTc)::value;
     constexpr bool CONST_STAGE = C::STAGE_UNROLL;
@@ -656,8 +663,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       // this step's loads (K(n+NS), V(n+NS-2)) go out behind the first MFMA,
       // so their address arithmetic overlaps the softmax
       if (j == 0) {
-        issue_k(n + NS, CONST_STAGE ? M : n % NS);
-        issue_v(n + NS - 2, CONST_STAGE ? (M + NS - 2) % NS : (n + NS - 2) % NS);
+        issue_k(n + NS, CONST_STAGE ? M : n % NS, CHECKc);
+        issue_v(n + NS - 2, CONST_STAGE ? (M + NS - 2) % NS : (n + NS - 2) % NS, CHECKc);
       }
       // issue order: this job's look-ahead reads, then its MFMA. Fma form:
       // the softmax instructions are left to the scheduler (pinning them
@@ -682,9 +689,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // ---- prologue: stages of K(0..NS-1) and V(0..NS-3) in flight, then all
   // published; S^T of tile 0 into sbuf[0].
 #pragma unroll
-  for (int n = 0; n < NS; ++n) issue_k(n, n);
+  for (int n = 0; n < NS; ++n) issue_k(n, n, True_{});
 #pragma unroll
-  for (int n = 0; n < NS - 2; ++n) issue_v(n, n);
+  for (int n = 0; n < NS - 2; ++n) issue_v(n, n, True_{});
   wait_vmcnt<0>();
   __syncthreads();
 #pragma unroll
@@ -698,22 +705,36 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // loaded meanwhile (their stages were last read in step n-1). At the end
   // each wave waits for all but the last NS-2 steps' loads, so K(n+2) and
   // V(n) are complete at the barrier.
-  step(0, std::integral_constant<int, 0>{}, True_{});
+  step(0, std::integral_constant<int, 0>{}, True_{}, True_{});
   if constexpr (C::STAGE_UNROLL) {
-    for (int n = 1; n < T; n += NS) {
+    int n = 1;
+    // iterations whose NS steps all exist (n + NS - 1 < T; under the causal
+    // mask T can be far below T_full) and that load only tiles ending inside
+    // the sequence (K up to n + 2NS - 1, V up to n + 2NS - 3, all < T_full):
+    // their loads need no clamping and no test for it. A loaded tile past
+    // the workgroup's last one (index T or more) goes to a stage no step
+    // reads, as the clamped reloads of the checked path do.
+    for (; n + NS <= T && n + 2 * NS - 1 < T_full; n += NS) {
+      static_for_steps<0, NS>([&](auto Ic) {
+        constexpr int i = decltype(Ic)::value;
+        step(n + i, std::integral_constant<int, (1 + i) % NS>{}, False_{}, False_{});
+        return true;
+      });
+    }
+    for (; n < T; n += NS) {
       const bool more = static_for_steps<0, NS>([&](auto Ic) {
         constexpr int i = decltype(Ic)::value;
         if (n + i >= T) return false;
-        step(n + i, std::integral_constant<int, (1 + i) % NS>{}, False_{});
+        step(n + i, std::integral_constant<int, (1 + i) % NS>{}, False_{}, True_{});
         return true;
       });
       if (!more) break;
     }
   } else {
     for (int n = 1; n < T; n += 2) {
-      step(n, std::integral_constant<int, 1>{}, False_{});
+      step(n, std::integral_constant<int, 1>{}, False_{}, True_{});
       if (n + 1 >= T) break;
-      step(n + 1, std::integral_constant<int, 0>{}, False_{});
+      step(n + 1, std::integral_constant<int, 0>{}, False_{}, True_{});
     }
   }
   // last tile T-1: its lazy-max check, then its P.V (V stage complete: waited
