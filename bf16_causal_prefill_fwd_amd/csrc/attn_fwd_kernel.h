@@ -334,11 +334,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   const int T_full = S / BN;
   const int k_tile_bytes = BN * k_stride32, v_tile_bytes = BN * v_stride32;
   const uint32_t k_lds_w = k_lds_addr + wave * 1024, v_lds_w = v_lds_addr + wave * 1024;
-  // CHECKc false: the caller guarantees n < T_full (no clamping of any kind)
+  // Unchecked loads (CHECKc false) run in the loop's unchecked part, whose
+  // tiles are all full and inside the sequence, one after the other: they
+  // take the tile from a running pointer (`next`, advanced by one tile per
+  // call) rather than from n.
   auto issue_tile = [&](const uint8_t* base, int tile_bytes, int stride, const int* loff, int nloads, int rowbytes,
-                        uint32_t dst, int n, auto CHECKc) {
+                        uint32_t dst, int n, auto CHECKc, const uint8_t*& next) {
     if constexpr (!decltype(CHECKc)::value) {
-      const uint8_t* tb = base + (int64_t)n * tile_bytes;
+      const uint8_t* tb = next;
+      next += tile_bytes;
 #pragma unroll
       for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst + i * C::NWAVES * 1024);
       return;
@@ -358,11 +362,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     }
   };
   // tile n into ring stage `stage` (= n % NS)
+  const uint8_t* k_next = kbase;  // next unchecked K / V tile
+  const uint8_t* v_next = vbase;
   auto issue_k = [&](int n, int stage, auto CHECKc) {
-    issue_tile(kbase, k_tile_bytes, k_stride32, k_loff, C::KLOADS, C::KROW, k_lds_w + stage * C::KTILE, n, CHECKc);
+    issue_tile(kbase, k_tile_bytes, k_stride32, k_loff, C::KLOADS, C::KROW, k_lds_w + stage * C::KTILE, n, CHECKc,
+               k_next);
   };
   auto issue_v = [&](int n, int stage, auto CHECKc) {
-    issue_tile(vbase, v_tile_bytes, v_stride32, v_loff, C::VLOADS, C::VROW, v_lds_w + stage * C::VTILE, n, CHECKc);
+    issue_tile(vbase, v_tile_bytes, v_stride32, v_loff, C::VLOADS, C::VROW, v_lds_w + stage * C::VTILE, n, CHECKc,
+               v_next);
   };
 
   // ---- per-lane LDS read offsets within a stage (the swizzle term depends
@@ -714,6 +722,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     // their loads need no clamping and no test for it. A loaded tile past
     // the workgroup's last one (index T or more) goes to a stage no step
     // reads, as the clamped reloads of the checked path do.
+    k_next = kbase + (int64_t)(n + NS) * k_tile_bytes;
+    v_next = vbase + (int64_t)(n + NS - 2) * v_tile_bytes;
     for (; n + NS <= T && n + 2 * NS - 1 < T_full; n += NS) {
       static_for_steps<0, NS>([&](auto Ic) {
         constexpr int i = decltype(Ic)::value;
@@ -731,7 +741,15 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       if (!more) break;
     }
   } else {
-    for (int n = 1; n < T; n += 2) {
+    int n = 1;
+    // unchecked part as above, two steps per iteration (K up to n + 1 + NS)
+    k_next = kbase + (int64_t)(n + NS) * k_tile_bytes;
+    v_next = vbase + (int64_t)(n + NS - 2) * v_tile_bytes;
+    for (; n + 2 <= T && n + 1 + NS < T_full; n += 2) {
+      step(n, std::integral_constant<int, 1>{}, False_{}, False_{});
+      step(n + 1, std::integral_constant<int, 0>{}, False_{}, False_{});
+    }
+    for (; n < T; n += 2) {
       step(n, std::integral_constant<int, 1>{}, False_{}, True_{});
       if (n + 1 >= T) break;
       step(n + 1, std::integral_constant<int, 0>{}, False_{}, True_{});
