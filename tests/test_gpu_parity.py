@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
 
-Bars (BASELINE tolerances): O relative L2 <= 3e-2 (FP8) / 5e-3 (BF16) over the
+Bars: O relative L2 <= 3e-2 (FP8) / 5e-3 (BF16) over the
 compared outputs, LSE max-abs error <= 1e-2, quantized codes and scales
 bit-exact, repeated launches bit-identical.
 
