@@ -210,13 +210,18 @@ def test_full_size_sampled_rows(name):
 
 # ---------------------------------------------------------------- tile-boundary sweep and exact-path stress
 
-BOUNDARY_S = [63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 320, 449]
+BOUNDARY_S = [63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 320, 449,
+              # the main loop's unchecked part (whole iterations of full tiles
+              # inside the sequence) starts at 9 full 64-key tiles: these run 0, 1
+              # and 2 such iterations with every length of the checked remainder
+              511, 512, 513, 575, 576, 577, 640, 705, 769, 831, 1024, 1087]
 
 
 @pytest.mark.parametrize("dtype", ["fp8", "bf16"])
 def test_sequence_lengths_around_tile_boundaries(dtype):
     # 64-key steps, 128-row workgroups, a main loop unrolled by the ring depth
-    # (4): these lengths give every tile count mod 4 and every ragged tail
+    # (4): these lengths give every tile count mod 4 and every ragged tail, in
+    # both parts of the main loop
     worst = (0.0, 0.0)
     for S in BOUNDARY_S:
         w = Workload(f"boundary_{S}", 1, S, 4, 2, 128, 128, dtype, "gauss")
