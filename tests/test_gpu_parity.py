@@ -235,6 +235,20 @@ def test_sequence_lengths_around_tile_boundaries(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_noncausal_through_the_unchecked_loop(dtype):
+    # non-causal rows walk every key tile, so these lengths also run the main
+    # loop's unchecked part, then a ragged checked remainder
+    for S in (577, 705, 1087):
+        w = Workload(f"noncausal_{S}", 1, S, 4, 2, 128, 128, dtype, "gauss", causal=False)
+        q, k, v, o, lse, ex = run_case(w, seed=S)
+        ref = prefill_reference(q, k, v, dtype, causal=False, fold_q=True)
+        err = rel_l2(o.float().cpu().numpy().astype(np.float64), ref["o"])
+        lerr = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref["lse"])))
+        print(f"  S={S}: O rel-L2 {err:.3e}  LSE max-abs {lerr:.3e}", flush=True)
+        assert err <= O_TOL[dtype] and lerr <= LSE_TOL, (S, err, lerr)
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
 def test_running_max_grows_every_tile(dtype):
     # scores rise with the key index (k_j = (0.5 + 2j/S) * u, q_i = 4 u for a
     # random unit-scale u), so each new tile holds the row's largest score
