@@ -59,6 +59,8 @@ SMALL = [
     Workload("batch4_xcd_order_bf16", 4, 100, 4, 2, 128, 128, "bf16", "gauss"),
     Workload("single_row_fp8", 1, 1, 2, 2, 128, 128, "fp8", "gauss"),
     Workload("ragged_mla_fp8", 1, 333, 4, 4, 192, 128, "fp8", "mla"),
+    # long enough for the MLA kernel's unchecked loop part (two-step loop)
+    Workload("mla_fp8_unchecked_loop", 1, 700, 2, 2, 192, 128, "fp8", "mla"),
     Workload("ragged_gqa_bf16", 1, 333, 8, 2, 128, 128, "bf16", "gauss"),
     Workload("batch2_bf16", 2, 129, 2, 2, 128, 128, "bf16", "gauss"),
     Workload("ragged_mla_bf16", 1, 200, 2, 2, 192, 128, "bf16", "mla"),
