@@ -137,11 +137,11 @@ int quantize_impl(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_s
 
 }  // namespace
 
-int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, hipStream_t stream) {
+int attn_quantize_fp8(const void* x, int x_dtype, uint8_t* x8, float* d_scale, int64_t n, hipStream_t stream) {
   return quantize_impl(x, x_dtype, n, x8, d_scale, nullptr, 0.f, 0, stream);
 }
 
-int attn_quantize_fp8_q(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale, const float* d_k_scale,
+int attn_quantize_fp8_q(const void* x, int x_dtype, uint8_t* x8, float* d_scale, int64_t n, const float* d_k_scale,
                         float softmax_scale, hipStream_t stream) {
   if (!d_k_scale) return ATTN_ERR_INVALID;
   return quantize_impl(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, 0, stream);
@@ -173,7 +173,7 @@ int attn_quantize_fp8_qkv(const void* q, const void* k, const void* v, int x_dty
              : ATTN_ERR_HIP;
 }
 
-int attn_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, int d, uint8_t* x8, float* d_scale,
+int attn_quantize_fp8_hadamard(const void* x, int x_dtype, uint8_t* x8, float* d_scale, int64_t n, int d,
                                const float* d_k_scale, float softmax_scale, hipStream_t stream) {
   if (d <= 0 || n <= 0 || n % d != 0) return ATTN_ERR_INVALID;
   const int block = (d & -d) < 128 ? (d & -d) : 128;
@@ -181,7 +181,7 @@ int attn_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, int d, uin
   return quantize_impl(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, block, stream);
 }
 
-int attn_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream) {
+int attn_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream) {
   if (!x || !y) return ATTN_ERR_INVALID;
   if (n <= 0 || n >= ((int64_t)1 << 40)) return ATTN_ERR_INVALID;
   if (((uintptr_t)x & 15u) || ((uintptr_t)y & 15u)) return ATTN_ERR_INVALID;
@@ -200,6 +200,6 @@ const char* attn_strerror(int code) {
   }
 }
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 }  // extern "C"

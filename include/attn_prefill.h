@@ -95,20 +95,28 @@ int attn_prefill_fwd_ex(const void* q, const void* k, const void* v, void* o, fl
 
 /*
  * Per-tensor FP8 quantize-and-layout step (the input side of the FP8 path).
- *   x        device input, n elements, float32 (x_dtype 0) or bfloat16 (1).
- *   n        element count, 0 < n < 2^40.
- *   x8       device output, n uint8 e4m3fn codes, same layout as x.
+ * The attention inputs are FP8 e4m3 (ai4bro.com, "TL;DR"; Le Fil IA, context
+ * paragraph: an e4m3 code read as an integer grows by 8 per doubling); the
+ * pages give no scale granularity, so this is one absmax scale per tensor.
+ *   x        device input, n elements, float32 (x_dtype 0) or bfloat16 (1),
+ *            16-byte aligned.
+ *   x8       device output, n uint8 e4m3fn codes, same layout as x, 16-byte
+ *            aligned.
  *   d_scale  device output, one float: absmax(|x|)/448 in fp32 (1.0 when x
  *            is all zeros). Also used as the absmax accumulator while the
- *            call's kernels run, so it must not alias x or x8.
+ *            call's kernels run, so it must not overlap x or x8.
+ *   n        element count, 0 < n < 2^40.
  * code = e4m3fn(x / scale), division in fp32 correctly rounded, rounding to
  * nearest with ties to even. Inputs must be finite. Deterministic.
+ * Errors: ATTN_ERR_INVALID for a null or misaligned pointer, a bad n or an
+ * overlap of d_scale with x or x8; ATTN_ERR_UNSUPPORTED for another x_dtype.
  */
-int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
+int attn_quantize_fp8(const void* x, int x_dtype, uint8_t* x8, float* d_scale, int64_t n,
                       hipStream_t stream);
 
 /*
- * The same step for a QUERY tensor, with the scale folded for the kernel:
+ * The same step for a QUERY tensor (same e4m3 format and sources), with the
+ * scale folded for the kernel; x, x_dtype, x8, d_scale, n as above:
  *   d_k_scale      device pointer to the key tensor's scale (one float,
  *                  e.g. the d_scale of attn_quantize_fp8 on k), read on
  *                  the device after the work queued before this call.
@@ -124,7 +132,7 @@ int attn_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x8, float*
  * detects this by itself; any other scale takes the general path). d_k_scale
  * must not overlap d_scale.
  */
-int attn_quantize_fp8_q(const void* x, int x_dtype, int64_t n, uint8_t* x8, float* d_scale,
+int attn_quantize_fp8_q(const void* x, int x_dtype, uint8_t* x8, float* d_scale, int64_t n,
                         const float* d_k_scale, float softmax_scale, hipStream_t stream);
 
 /*
@@ -150,7 +158,7 @@ int attn_quantize_fp8_qkv(const void* q, const void* k, const void* v, int x_dty
  * K (aicronaca.it, section "Perché l'FP8 non basta da solo": rotating Q and K
  * before the FP8 cast about halves the input quantization error). V is not
  * rotated.
- *   x, x_dtype, n, x8, d_scale   as attn_quantize_fp8; x is rows of d elements.
+ *   x, x_dtype, x8, d_scale, n   as attn_quantize_fp8; x is rows of d elements.
  *   d          head dim, the length of the last axis (n % d == 0). Rotation
  *              blocks of b = largest power of two dividing d, at most 128,
  *              must be 64 or 128 (d = 128: one block; d = 192: three of 64),
@@ -167,19 +175,22 @@ int attn_quantize_fp8_qkv(const void* q, const void* k, const void* v, int x_dty
  * products are then the unrotated q.k, and the query keeps the folded
  * property, so the attention call needs no change. Deterministic.
  */
-int attn_quantize_fp8_hadamard(const void* x, int x_dtype, int64_t n, int d, uint8_t* x8, float* d_scale,
+int attn_quantize_fp8_hadamard(const void* x, int x_dtype, uint8_t* x8, float* d_scale, int64_t n, int d,
                                const float* d_k_scale, float softmax_scale, hipStream_t stream);
 
 /*
- * BF16 input step: float32 -> bfloat16, round to nearest, ties to even.
- *   x  device float32[n];  y  device bfloat16[n] (as uint16 bits);  0 < n < 2^40.
+ * BF16 input step: float32 -> bfloat16, round to nearest, ties to even (the
+ * BF16 path takes its inputs unquantized: Le Fil IA, summary paragraph).
+ *   x  device float32[n];  y  device bfloat16[n] (as uint16 bits), both
+ *   16-byte aligned;  0 < n < 2^40.  Errors: ATTN_ERR_INVALID.
  */
-int attn_cast_bf16(const float* x, int64_t n, uint16_t* y, hipStream_t stream);
+int attn_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream);
 
 /* Human-readable text of a return code (static storage). */
 const char* attn_strerror(int code);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (2: quantizers take (x, x_dtype, x8, d_scale, n, ...),
+ * the cast (x, y, n, ...)). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

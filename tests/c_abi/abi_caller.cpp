@@ -132,9 +132,9 @@ int main() {
   const float sm = 1.0f / sqrtf((float)D);
 
   // ---- FP8: K and V quantized, then Q with the folded scale; scales stay on the device
-  ATTN_OK_(attn_quantize_fp8(dk, 0, (int64_t)nkv, k8, dscales + 1, st));
-  ATTN_OK_(attn_quantize_fp8(dv, 0, (int64_t)nkv, v8, dscales + 2, st));
-  ATTN_OK_(attn_quantize_fp8_q(dq, 0, (int64_t)nq, q8, dscales, dscales + 1, sm, st));
+  ATTN_OK_(attn_quantize_fp8(dk, 0, k8, dscales + 1, (int64_t)nkv, st));
+  ATTN_OK_(attn_quantize_fp8(dv, 0, v8, dscales + 2, (int64_t)nkv, st));
+  ATTN_OK_(attn_quantize_fp8_q(dq, 0, q8, dscales, (int64_t)nq, dscales + 1, sm, st));
   ATTN_OK_(attn_prefill_fwd_ex(q8, k8, v8, dout, dlse, 1.f, 1.f, 1.f, dscales, sm, B, S, HQ, HKV, D, D, 1,
                                ATTN_DTYPE_FP8_E4M3, st));
   std::vector<uint8_t> hv8(nkv);
@@ -148,9 +148,9 @@ int main() {
   if (check("fp8", o, lse, vdeq)) return 1;
 
   // ---- BF16: RNE casts, then the same closed form
-  ATTN_OK_(attn_cast_bf16(dq, (int64_t)nq, qb, st));
-  ATTN_OK_(attn_cast_bf16(dk, (int64_t)nkv, kb, st));
-  ATTN_OK_(attn_cast_bf16(dv, (int64_t)nkv, vb, st));
+  ATTN_OK_(attn_cast_bf16(dq, qb, (int64_t)nq, st));
+  ATTN_OK_(attn_cast_bf16(dk, kb, (int64_t)nkv, st));
+  ATTN_OK_(attn_cast_bf16(dv, vb, (int64_t)nkv, st));
   ATTN_OK_(attn_prefill_fwd(qb, kb, vb, dout, dlse, 1.f, 1.f, 1.f, B, S, HQ, HKV, D, D, 1, ATTN_DTYPE_BF16, st));
   std::vector<uint16_t> hvb(nkv);
   HIP_OK(hipMemcpyAsync(hvb.data(), vb, nkv * 2, hipMemcpyDeviceToHost, st));

@@ -1,0 +1,76 @@
+"""How exactly the FP8 matrix core sums a Q.K dot product, read through the
+attention kernel itself.
+
+With one key per row (S = 1) the softmax has a single term: p = 1, l = 1,
+and the kernel's LSE is ln 2 * t, where t is the row's score in log2 units as
+the scaled FP8 MFMA hands it over. Codes are passed directly (no input step)
+with q_scale = k_scale = 1 and softmax_scale = fp32(ln 2), so the score factor
+q_scale * k_scale * softmax_scale * log2(e) rounds to 1 and the kernel takes
+its folded form with an operand scale of 2^0: t is the MFMA's sum of the
+e4m3 products, chained over the 64-deep contraction steps in fp32. Every
+product of two e4m3 values is exact in fp32, so a correctly rounded fp32
+accumulation would be off by at most a few units of 2^-24 of the sum of the
+absolute products. The test measures the actual error against the exact
+(fp64) dot product of the same codes, for Gaussian operands and for operands
+where one product (448 * 448) dominates, as it does when an outlier channel
+of Q meets one of K in the heavy-tailed layer.
+
+What it pins: the error bound quoted in the design notes for the LSE error of
+the heavy-tailed layer (at most 2^-13 of the sum of |products| per score).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from bf16_causal_prefill_fwd_amd import ops
+from oracle import e4m3fn_decode, e4m3fn_encode
+
+pytestmark = pytest.mark.gpu
+
+LN2_F32 = float(np.float32(math.log(2.0)))
+
+
+def _codes(rng, shape, scale):
+    return e4m3fn_encode(np.float32(rng.standard_normal(shape) * scale))
+
+
+def _case(d_qk: int, dominant: bool, seed: int, H: int = 2048):
+    rng = np.random.default_rng(seed)
+    q = _codes(rng, (1, 1, H, d_qk), 48.0)
+    k = _codes(rng, (1, 1, H, d_qk), 48.0)
+    if dominant:
+        # one channel per head holds the largest e4m3 value in both q and k
+        ch = rng.integers(0, d_qk, H)
+        big = e4m3fn_encode(np.float32([448.0]))[0]
+        q[0, 0, np.arange(H), ch] = big
+        k[0, 0, np.arange(H), ch] = big
+    return q, k
+
+
+@pytest.mark.parametrize("d_qk", [128, 192])
+def test_fp8_mfma_dot_product_error(d_qk):
+    worst = {}
+    for dominant in (False, True):
+        q, k = _case(d_qk, dominant, seed=7 + d_qk + int(dominant))
+        H = q.shape[2]
+        v = np.full((1, 1, H, 128), e4m3fn_encode(np.float32([1.0]))[0], dtype=np.uint8)
+        print(f"case mfma precision d_qk={d_qk} dominant={dominant} H={H}", flush=True)
+        qd, kd, vd = (torch.from_numpy(x).to("cuda") for x in (q, k, v))
+        o, lse = ops.attn_prefill_fwd(qd, kd, vd, 1.0, 1.0, 1.0, causal=True, softmax_scale=LN2_F32)
+        torch.cuda.synchronize()
+        t = lse.cpu().numpy().astype(np.float64)[0, :, 0] / LN2_F32
+        prod = e4m3fn_decode(q[0, 0]) * e4m3fn_decode(k[0, 0])  # [H, d_qk], exact in fp64
+        exact = prod.sum(axis=1)
+        mag = np.abs(prod).sum(axis=1)
+        # the LSE's own fp32 rounding (ln 2 * t, then / ln 2 here) is 2^-24 of |t|
+        rel = np.abs(t - exact) / mag
+        worst[dominant] = float(rel.max())
+        print(f"  max |t - exact| / sum|products| = 2^{math.log2(max(worst[dominant], 1e-30)):.2f} "
+              f"(median 2^{math.log2(max(float(np.median(rel)), 1e-30)):.2f})", flush=True)
+        assert np.all(np.isfinite(t))
+        # O of a single key is that key's V row (1.0) exactly
+        assert torch.all(o == 1.0).item()
+    assert worst[False] <= 2.0 ** -13 and worst[True] <= 2.0 ** -13, worst

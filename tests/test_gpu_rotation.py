@@ -5,8 +5,8 @@ codes and stored scales bit-exact (both sides decide the codes from fp64
 rotated values), for keys and folded queries, fp32 and bf16 inputs, head dims
 128 and 192, ragged row counts, a single row, an all-zero tensor and a
 one-hot row. Then the whole path with the rotation against the oracle on the
-same rotated inputs (O rel-L2 <= 3e-2, LSE max-abs <= 1e-2, repeat launches
-bit-identical). The end-to-end error against fp64 attention on the
+same rotated inputs (O rel-L2 <= 3e-2 over the tensor and the per-row bar of
+parity_util.py, LSE max-abs <= 1e-2, repeat launches bit-identical). The end-to-end error against fp64 attention on the
 unquantized inputs must drop on inputs whose large channels Q and K share,
 which is the effect the pages report (aicronaca.it, section "Perché l'FP8 non
 basta da solo"). Last, the full-size GQA layer: whole Q and K code tensors
@@ -26,15 +26,11 @@ from oracle.rotation import hadamard_quantize
 
 pytestmark = pytest.mark.gpu
 
-O_TOL, LSE_TOL = 3e-2, 1e-2
+from .parity_util import LSE_TOL, check_o, rel_l2  # noqa: E402
 
 
 def dev(x: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
-
-
-def rel_l2(got, ref) -> float:
-    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
 
 
 def _input(shape, xdtype, seed):
@@ -116,10 +112,10 @@ def test_rotated_path_matches_oracle(w):
     assert np.array_equal(sc, np.float32([ref["q_scale"], ref["k_scale"], ref["v_scale"]]))
     og = o.float().cpu().numpy().astype(np.float64)
     lg = lse.cpu().numpy().astype(np.float64)
-    err = rel_l2(og, ref["o"])
+    check_o(og, ref["o"], "fp8")
     lerr = float(np.max(np.abs(lg - ref["lse"])))
-    print(f"  O rel-L2 {err:.3e}  LSE max-abs {lerr:.3e}", flush=True)
-    assert err <= O_TOL and lerr <= LSE_TOL
+    print(f"  LSE max-abs {lerr:.3e}", flush=True)
+    assert lerr <= LSE_TOL
     o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], causal=w.causal, d_scales=ex["scales"])
     assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(l2, lse)
 
@@ -160,7 +156,7 @@ def test_full_size_gqa_rotated():
     ii = torch.tensor([r[2] for r in rows])
     og = o[bi, ii, hi].float().cpu().numpy().astype(np.float64)
     lg = lse[bi, hi, ii].cpu().numpy().astype(np.float64)
-    err = rel_l2(og, ref["o_rows"])
+    check_o(og, ref["o_rows"], "fp8", f"{len(rows)} rows: ")
     lerr = float(np.max(np.abs(lg - ref["lse_rows"])))
-    print(f"  {len(rows)} rows: O rel-L2 {err:.3e}  LSE max-abs {lerr:.3e}", flush=True)
-    assert err <= O_TOL and lerr <= LSE_TOL
+    print(f"  LSE max-abs {lerr:.3e}", flush=True)
+    assert lerr <= LSE_TOL
