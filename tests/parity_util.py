@@ -14,14 +14,17 @@ those rounding errors, up to the correlation of the few V rows that dominate
 it (about 1/sqrt(d_v) = 9% for d_v = 128), plus the bf16 rounding of the
 output (2^-9). Probabilities far below the running maximum are e4m3
 subnormals, whose absolute spacing 2^-9 is coarser; rows carried mostly by
-such small probabilities sit higher. ROW_TOL bounds the measured maximum over
-every parity case with a margin; a wrong row lands near sqrt(2).
+such small probabilities sit higher. So the FP8 bar is 2^-4 * 1.25 plus the
+output rounding, 0.08, and the BF16 bar 2^-9 * 2.5 plus the output rounding,
+0.008. The largest row errors measured over every GPU parity case are 0.061
+(FP8, 6,216-row heavy-tailed GQA case, plain query scale) and 0.0044 (BF16,
+non-causal MLA). A wrong row lands near sqrt(2).
 """
 
 import numpy as np
 
 O_TOL = {"fp8": 3e-2, "bf16": 5e-3}
-ROW_TOL = {"fp8": 0.12, "bf16": 0.012}
+ROW_TOL = {"fp8": 0.08, "bf16": 0.008}
 LSE_TOL = 1e-2
 
 

@@ -15,8 +15,11 @@ absolute products. The test measures the actual error against the exact
 where one product (448 * 448) dominates, as it does when an outlier channel
 of Q meets one of K in the heavy-tailed layer.
 
-What it pins: the error bound quoted in the design notes for the LSE error of
-the heavy-tailed layer (at most 2^-13 of the sum of |products| per score).
+What it pins, for the LSE error of the heavy-tailed layer: the matrix core
+does not accumulate in full fp32 (errors far above the few units of 2^-24 an
+fp32 sum would leave; measured 2^-16.7 of the sum of |products| for Gaussian
+operands and 2^-14.1 with one dominant product), and the error stays within
+2^-13.5 of that sum.
 """
 
 import math
@@ -73,4 +76,7 @@ def test_fp8_mfma_dot_product_error(d_qk):
         assert np.all(np.isfinite(t))
         # O of a single key is that key's V row (1.0) exactly
         assert torch.all(o == 1.0).item()
-    assert worst[False] <= 2.0 ** -13 and worst[True] <= 2.0 ** -13, worst
+    assert worst[False] <= 2.0 ** -15 and worst[True] <= 2.0 ** -13.5, worst
+    # a correctly rounded fp32 accumulation of exact products, chained over
+    # two or three MFMAs, is off by at most ~3 * 2^-24 of the sum of |products|
+    assert worst[True] >= 2.0 ** -20, worst
