@@ -256,6 +256,8 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--hadamard", action="store_true",
                     help="FP8: rotate Q and K by Hadamard blocks in the input step (attn_quantize_fp8_hadamard)")
+    ap.add_argument("--p-block-scale", action="store_true",
+                    help="FP8: per (row, 64-key block) power-of-two scaling of P (ATTN_FLAG_P_BLOCK_SCALE)")
     ap.add_argument("--seq-len", type=int, default=None, help="override the workload's sequence length")
     ap.add_argument("--heads", type=int, default=None,
                     help="override the head count: Hq = Hkv = HEADS (multi-head attention)")
@@ -319,9 +321,10 @@ def main(argv=None) -> int:
 
     sm_scale = 1.0 / math.sqrt(w.d_qk)
 
-    if args.hadamard and w.dtype != "fp8":
-        print("--hadamard applies to FP8 workloads only", file=sys.stderr)
+    if (args.hadamard or args.p_block_scale) and w.dtype != "fp8":
+        print("--hadamard and --p-block-scale apply to FP8 workloads only", file=sys.stderr)
         return 2
+    flags = ops.ATTN_FLAG_P_BLOCK_SCALE if args.p_block_scale else 0
 
     def input_step():
         if w.dtype == "fp8" and not args.hadamard:
@@ -339,7 +342,8 @@ def main(argv=None) -> int:
 
     def attention():
         if w.dtype == "fp8":
-            ops.attn_prefill_fwd(*codes, causal=w.causal, out=o, lse=lse, d_scales=scales, stream=stream)
+            ops.attn_prefill_fwd(*codes, causal=w.causal, out=o, lse=lse, d_scales=scales, stream=stream,
+                                 flags=flags)
         else:
             ops.attn_prefill_fwd(*codes, causal=w.causal, out=o, lse=lse, stream=stream)
 
@@ -404,7 +408,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "d_qk": w.d_qk,
                    "d_v": w.d_v, "causal": w.causal, "dist": w.dist, "seed": args.seed,
-                   "hadamard": bool(args.hadamard),
+                   "hadamard": bool(args.hadamard), "p_block_scale": bool(args.p_block_scale),
                    "step": "input step (quantize/cast Q,K,V) + attention"},
         "attention_ms": round(attn_avg, 4),
         "attention_ms_min": round(float(np.min(attn_ms)), 4),

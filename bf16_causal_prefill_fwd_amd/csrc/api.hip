@@ -40,7 +40,7 @@ bool good_scale(float s) { return isfinite(s) && s > 0.f; }
 
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale, float k_scale,
              float v_scale, const float* d_scales, float softmax_scale, int B, int S, int Hq, int Hkv, int d_qk,
-             int d_v, int causal, int dtype, hipStream_t stream) {
+             int d_v, int causal, int dtype, int flags, hipStream_t stream) {
   // ---- host-side checks, before any HIP call
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID;
   if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || d_qk <= 0 || d_v <= 0) return ATTN_ERR_INVALID;
@@ -56,8 +56,11 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, f
     return ATTN_ERR_INVALID;
   const double elems = (double)B * S * Hq * (d_qk > d_v ? d_qk : d_v);
   if (elems >= 1099511627776.0) return ATTN_ERR_INVALID;
+  if (flags & ~ATTN_FLAG_P_BLOCK_SCALE) return ATTN_ERR_INVALID;
   if (dtype != ATTN_DTYPE_FP8_E4M3 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
   if (!((d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128))) return ATTN_ERR_UNSUPPORTED;
+  if (flags && dtype != ATTN_DTYPE_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
+  const int pmode = (flags & ATTN_FLAG_P_BLOCK_SCALE) ? kPBlockScaled : kPExact;
 
   const int ready = device_ready();
   if (ready != ATTN_OK) return ready;
@@ -79,7 +82,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, f
   prm.Hkv = Hkv;
   prm.causal = causal;
 
-  switch (launch_attn_fwd(prm, dtype == ATTN_DTYPE_FP8_E4M3, d_qk, stream)) {
+  switch (launch_attn_fwd(prm, dtype == ATTN_DTYPE_FP8_E4M3, d_qk, pmode, stream)) {
     case kLaunched: return ATTN_OK;
     case kTooManyWorkgroups: return ATTN_ERR_INVALID;
     default: return ATTN_ERR_HIP;
@@ -96,15 +99,15 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
                      int dtype, hipStream_t stream) {
   const float sm = d_qk > 0 ? (float)(1.0 / sqrt((double)d_qk)) : 0.f;
   return attn::fwd_impl(q, k, v, o, lse, q_scale, k_scale, v_scale, nullptr, sm, B, S, Hq, Hkv, d_qk, d_v,
-                        causal, dtype, stream);
+                        causal, dtype, 0, stream);
 }
 
 int attn_prefill_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, float q_scale,
                         float k_scale, float v_scale, const float* d_scales, float softmax_scale, int B, int S,
-                        int Hq, int Hkv, int d_qk, int d_v, int causal, int dtype, hipStream_t stream) {
+                        int Hq, int Hkv, int d_qk, int d_v, int causal, int dtype, int flags, hipStream_t stream) {
   if (d_scales && ((uintptr_t)d_scales & 3u)) return ATTN_ERR_INVALID;
   return attn::fwd_impl(q, k, v, o, lse, q_scale, k_scale, v_scale, d_scales, softmax_scale, B, S, Hq, Hkv, d_qk,
-                        d_v, causal, dtype, stream);
+                        d_v, causal, dtype, flags, stream);
 }
 
 namespace {

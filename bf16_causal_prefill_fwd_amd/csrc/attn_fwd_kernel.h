@@ -228,7 +228,22 @@ __device__ __forceinline__ bool static_for_steps(F&& f) {
 
 enum ScoreForm { kScaleFma = 0, kScaleFolded = 1 };
 
-template <class C, int FORM>
+// How probabilities reach the P.V MFMA.
+//  * kPExact: P = e4m3 (FP8) or bf16 rounding of p, the exact exp2.
+//  * kPBlockScaled (FP8): per (query row, 64-key block), P = e4m3(p * 2^kb)
+//    with an integer kb >= 0, and the P.V MFMA multiplies its products by
+//    2^-kb through the E8M0 operand scale of P, so O is unchanged up to the
+//    rounding; small probabilities keep normal e4m3 precision instead of
+//    falling into the subnormal range (aicronaca.it, "Perché l'FP8 non basta
+//    da solo"; ai4bro.com, "How does ZYFA work?": power-of-two scaling of
+//    each 64-key block of P, absorbed by the scaled MFMA).
+enum PMode { kPExact = 0, kPBlockScaled = 1 };
+
+// Largest block shift: 2^-kMaxShift stays a normal fp32 and 127 - kMaxShift
+// a valid E8M0 scale.
+constexpr int kMaxShift = 100;
+
+template <class C, int FORM, int PM>
 __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, char* v_ring, float vs,
                                               float c_log2, int kc) {
   const ATTN_LDS char* k_lds = (const ATTN_LDS char*)k_ring;
@@ -237,6 +252,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   const uint32_t v_lds_addr = lds_address(v_ring);
   constexpr bool FOLD = FORM == kScaleFolded;
   static_assert(!FOLD || C::FP8, "scale folding needs the scaled FP8 MFMA");
+  constexpr bool PS = PM == kPBlockScaled;
+  static_assert(!PS || C::FP8, "block-scaled P needs the scaled FP8 MFMA");
+  // scaled MFMAs are not matched by scheduling groups: fences order the jobs
+  constexpr bool FENCED = FOLD || PS;
 
   constexpr int BN = C::BN, DV = C::DV, NS = C::NSTAGE;
   const int tid = threadIdx.x;
@@ -416,6 +435,22 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   float m_run = FOLD ? 0.f : -1e30f;
   float l_run = 0.f;  // this lane's share of the running row sum
   f32x16 cblk = f32x16{};
+  // Block-scaled P: kb_div = 2^-kb for the shift kb of the tile being
+  // converted (the same for the two lanes of a query, which hold the two
+  // halves of its 64-key block; kb_div is the divisor of the scaled
+  // conversion), and by tile parity the E8M0 scale 127 - kb that the tile's
+  // P.V MFMA applies, which is kb_div's exponent field. Each block's shift
+  // comes from its own largest probability 2^lg (taken from its scores
+  // before any of them is converted): kb = 7 - floor(lg), at least 0, maps
+  // it into [128, 256), below the e4m3 maximum 448; a larger probability
+  // (lg >= 8) takes kb = 0, and its block the exact path. fmed3 keeps
+  // lg = -inf (every key of the block hidden from the lane's query) at the
+  // largest shift, where its zeros stay zeros.
+  float kb_div = 1.f;
+  int e8[2] = {127, 127};
+  auto set_shift = [&](float lg) {
+    if constexpr (PS) kb_div = pow2i((int)__builtin_amdgcn_fmed3f(floorf(lg) - 7.f, (float)-kMaxShift, 0.f));
+  };
 
   // Scores and P operands are double-buffered by tile parity: step n reads
   // the scores of tile n from sbuf[n&1] and writes tile n+1's into
@@ -480,7 +515,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       const int tv = j % C::NOT, u = j / C::NOT;
       if constexpr (C::FP8) {
         i32x8 pop = {pv[0][0], pv[0][1], pv[0][2], pv[0][3], pv[1][0], pv[1][1], pv[1][2], pv[1][3]};
-        oacc[tv] = mfma_f8(a, pop, oacc[tv]);
+        oacc[tv] = PS ? mfma_f8_scaled(a, pop, oacc[tv], 127, e8[PP]) : mfma_f8(a, pop, oacc[tv]);
       } else {
         oacc[tv] = mfma_bf16(__builtin_bit_cast(bf16x8, a), pv[u], oacc[tv]);
       }
@@ -536,8 +571,13 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       // dword (c & 3) of pout[t]
       // (both halves are written: the register's old contents only save an
       // instruction that would clear it)
-      const int x = cvt_fp8x2(p0, p1, pout[t][c & 3], false);
-      pout[t][c & 3] = pin(cvt_fp8x2(p2, p3, x, true));
+      if constexpr (PS) {
+        const int x = cvt_fp8x2_div(p0, p1, kb_div, pout[t][c & 3], false);
+        pout[t][c & 3] = pin(cvt_fp8x2_div(p2, p3, kb_div, x, true));
+      } else {
+        const int x = cvt_fp8x2(p0, p1, pout[t][c & 3], false);
+        pout[t][c & 3] = pin(cvt_fp8x2(p2, p3, x, true));
+      }
     } else {
       // BF16 operand u = 2t + (r / 8) holds registers 8(u%2) .. +7 of tile t
       const int u = 2 * t + (r >> 3), e = r & 7;
@@ -568,9 +608,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[t][r], sc[t][r + 1]));
     mx = fmaxf(mx, swap_halves(mx));
+    // (block-scaled P: the block's largest probability after the update is
+    // 2^lg, lg <= 0)
     if constexpr (!FOLD) {
       const float m_new = fmaxf(m_run, mx * c_log2);
       const float alpha = fast_exp2(m_run - m_new);
+      set_shift(mx * c_log2 - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -583,6 +626,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       // always sees key 0 there, so mx is finite)
       const float d = first ? mx : fmaxf(mx, 0.f);
       const float alpha = first ? 0.f : fast_exp2(-d);
+      set_shift(mx - d);
       m_run += d;
       l_run *= alpha;
 #pragma unroll
@@ -629,6 +673,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
         }
       }
     }
+    // block-scaled P: the shift of tile n from its largest score
+    if constexpr (PS) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < C::NST; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sbuf[P][t][r], sbuf[P][t][r + 1]));
+      mx = fmaxf(mx, swap_halves(mx));
+      set_shift(FOLD ? mx : mx * c_log2 - m_run);
+    }
     // V(n-1) sits in stage (n-1) % NS; at n = 0 P is zero and stage 0 (V(0)) is read
     const int vst = FIRST ? 0 : (CONST_STAGE ? (M + NS - 1) % NS : (n - 1) % NS);
     const int kst = CONST_STAGE ? (M + 1) % NS : (n + 1) % NS;
@@ -666,7 +720,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
           probs_chunk(c, Pc{}, m_run, lsum, False_{});
         }
       }
-      if constexpr (FOLD) sched_fence();
+      if constexpr (FENCED) sched_fence();
       run_job(job_at(j), fr[j % (LA + 1)], std::integral_constant<int, Q>{}, std::integral_constant<int, Q>{});
       // this step's loads (K(n+NS), V(n+NS-2)) go out behind the first MFMA,
       // so their address arithmetic overlaps the softmax
@@ -678,7 +732,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       // the softmax instructions are left to the scheduler (pinning them
       // measured slower). Folded form: the scaled MFMA is not matched by
       // scheduling groups, so fences keep each job's chunk ahead of its MFMA
-      if constexpr (FOLD) {
+      if constexpr (FENCED) {
         sched_fence();
       } else {
         if (j + LA < NJOB) sched_group<kSchedDsRead>(frag_reads(job_at(j + LA)));
@@ -692,6 +746,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     const bool first = FOLD && FIRST;
     if (wave_any(first | !(lsum <= kLazyMaxThreshold))) exact_path(Pc{}, lsum, first);
     l_run += lsum;
+    if constexpr (PS) e8[P] = __float_as_int(kb_div) >> 23;  // 127 - kb, for tile n's P.V in step n + 1
   };
 
   // ---- prologue: stages of K(0..NS-1) and V(0..NS-3) in flight, then all
@@ -796,7 +851,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   }
 }
 
-template <class C>
+template <class C, int PM>
 __global__ __launch_bounds__(C::NTHREADS, C::WG_PER_CU) void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) char k_ring[C::NSTAGE * C::KTILE];
   __shared__ __attribute__((aligned(1024))) char v_ring[C::NSTAGE * C::VTILE];
@@ -815,11 +870,11 @@ __global__ __launch_bounds__(C::NTHREADS, C::WG_PER_CU) void attn_fwd_kernel(Fwd
     const float f = frexpf(c_log2, &e);
     const bool pow2 = fabsf(f - 0.5f) <= 0x1p-19f || fabsf(f - 1.0f) <= 0x1p-18f;
     if (uniform(pow2 ? 1 : 0)) {
-      attn_fwd_body<C, kScaleFolded>(p, k_ring, v_ring, vs, c_log2, uniform(f < 0.75f ? e - 1 : e));
+      attn_fwd_body<C, kScaleFolded, PM>(p, k_ring, v_ring, vs, c_log2, uniform(f < 0.75f ? e - 1 : e));
       return;
     }
   }
-  attn_fwd_body<C, kScaleFma>(p, k_ring, v_ring, vs, c_log2, 0);
+  attn_fwd_body<C, kScaleFma, PM>(p, k_ring, v_ring, vs, c_log2, 0);
 }
 
 }  // namespace attn

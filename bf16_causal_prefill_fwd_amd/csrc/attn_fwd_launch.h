@@ -15,21 +15,26 @@ enum LaunchStatus { kLaunched = 0, kTooManyWorkgroups = 1, kLaunchFailed = 2 };
 
 // One workgroup per (batch, query head, query tile); the XCD-aware order
 // needs the (batch, kv head) units to split evenly over the 8 XCDs.
-template <class C>
+template <class C, int PM>
 inline LaunchStatus launch_fwd(FwdParams prm, hipStream_t stream) {
   prm.n_mtiles = (prm.S + C::BM - 1) / C::BM;
   const int64_t units = (int64_t)prm.B * prm.Hkv;
   const int64_t items = (int64_t)prm.B * prm.Hq * prm.n_mtiles;
   if (items > 0x7FFFFFFF) return kTooManyWorkgroups;
   prm.xcd_remap = (units % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(attn_fwd_kernel<C>, dim3((unsigned)items), dim3(C::NTHREADS), 0, stream, prm);
+  hipLaunchKernelGGL((attn_fwd_kernel<C, PM>), dim3((unsigned)items), dim3(C::NTHREADS), 0, stream, prm);
   return hipGetLastError() == hipSuccess ? kLaunched : kLaunchFailed;
 }
 
-// d_qk is 128 or 192 (d_v 128), checked by the caller.
-inline LaunchStatus launch_attn_fwd(FwdParams prm, bool fp8, int d_qk, hipStream_t stream) {
-  if (fp8) return d_qk == 128 ? launch_fwd<CfgF8D128>(prm, stream) : launch_fwd<CfgF8D192>(prm, stream);
-  return d_qk == 128 ? launch_fwd<CfgBFD128>(prm, stream) : launch_fwd<CfgBFD192>(prm, stream);
+// d_qk is 128 or 192 (d_v 128), and pmode kPExact for BF16, checked by the
+// caller.
+inline LaunchStatus launch_attn_fwd(FwdParams prm, bool fp8, int d_qk, int pmode, hipStream_t stream) {
+  if (fp8 && pmode == kPBlockScaled)
+    return d_qk == 128 ? launch_fwd<CfgF8D128, kPBlockScaled>(prm, stream)
+                       : launch_fwd<CfgF8D192, kPBlockScaled>(prm, stream);
+  if (fp8)
+    return d_qk == 128 ? launch_fwd<CfgF8D128, kPExact>(prm, stream) : launch_fwd<CfgF8D192, kPExact>(prm, stream);
+  return d_qk == 128 ? launch_fwd<CfgBFD128, kPExact>(prm, stream) : launch_fwd<CfgBFD192, kPExact>(prm, stream);
 }
 
 }  // namespace attn

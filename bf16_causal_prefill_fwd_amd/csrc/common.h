@@ -75,6 +75,19 @@ __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old, bool hi) {
             : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
 }
 
+// As cvt_fp8x2, of a / div and b / div (one rounding, to nearest even; div
+// a power of two here, so this scales by an exact power of two first).
+// Values past the e4m3 range give NaN codes: callers keep them in range.
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ int cvt_fp8x2_div(float a, float b, float div, int old, bool hi) {
+  const i16x2 o = __builtin_bit_cast(i16x2, old);
+  return __builtin_bit_cast(int, hi ? __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, div, true)
+                                    : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, div, false));
+}
+
+// fp32 2^e for an integer e in [-126, 127] (built from the exponent field).
+__device__ __forceinline__ float pow2i(int e) { return __int_as_float((e + 127) << 23); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Byte address of an LDS object (what M0 and ds_* address operands hold).

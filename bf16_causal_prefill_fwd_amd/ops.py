@@ -20,6 +20,7 @@ from .build import LIB_PATH, INCLUDE
 ATTN_OK = 0
 ATTN_DTYPE_FP8_E4M3 = 0
 ATTN_DTYPE_BF16 = 1
+ATTN_FLAG_P_BLOCK_SCALE = 1
 
 _lib = None
 
@@ -36,7 +37,7 @@ _SIGNATURES = {
     "attn_prefill_fwd_ex": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                      _c_float, _c_float, _c_float, _c_void_p, _c_float,
                                      _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                     _c_void_p]),
+                                     _c_int, _c_void_p]),
     "attn_quantize_fp8": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_int64, _c_void_p]),
     "attn_quantize_fp8_q": (_c_int, [_c_void_p, _c_int, _c_void_p, _c_void_p, _c_int64, _c_void_p, _c_float,
                                      _c_void_p]),
@@ -308,9 +309,10 @@ def check_attention_args(q, k, v, out=None, lse=None, d_scales=None):
 
 
 def attn_prefill_fwd(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True, out=None, lse=None,
-                     return_lse=True, softmax_scale=None, d_scales=None, stream=None):
+                     return_lse=True, softmax_scale=None, d_scales=None, stream=None, flags: int = 0):
     """Causal prefill attention forward through the C ABI (attn_prefill_fwd,
-    or attn_prefill_fwd_ex when ``d_scales`` or ``softmax_scale`` is given).
+    or attn_prefill_fwd_ex when ``d_scales``, ``softmax_scale`` or ``flags``
+    is given; ``flags``: ATTN_FLAG_* bits).
 
     q [B,S,Hq,d_qk], k [B,S,Hkv,d_qk], v [B,S,Hkv,d_v] device tensors (FP8
     codes as uint8/float8_e4m3fn, or bfloat16). Returns (o bf16 [B,S,Hq,d_v],
@@ -324,7 +326,7 @@ def attn_prefill_fwd(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     L = lib()
-    if d_scales is None and softmax_scale is None:
+    if d_scales is None and softmax_scale is None and not flags:
         code = L.attn_prefill_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
                                   float(q_scale), float(k_scale), float(v_scale),
                                   B, S, Hq, Hkv, dqk, dv, int(bool(causal)), dt, _stream(stream))
@@ -333,7 +335,7 @@ def attn_prefill_fwd(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True
         sm = 1.0 / math.sqrt(dqk) if softmax_scale is None else float(softmax_scale)
         code = L.attn_prefill_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse),
                                      float(q_scale), float(k_scale), float(v_scale), _ptr(d_scales), sm,
-                                     B, S, Hq, Hkv, dqk, dv, int(bool(causal)), dt, _stream(stream))
+                                     B, S, Hq, Hkv, dqk, dv, int(bool(causal)), dt, int(flags), _stream(stream))
         _check("attn_prefill_fwd_ex", code)
     return out, lse
 
@@ -347,21 +349,21 @@ def attn_prefill(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True):
 
 
 def prefill(q32: torch.Tensor, k32: torch.Tensor, v32: torch.Tensor, dtype: str = "fp8", causal=True,
-            stream=None, fold_q: bool = True, hadamard: bool = False):
+            stream=None, fold_q: bool = True, hadamard: bool = False, flags: int = 0):
     """The whole path on float32 device inputs: input step, then attention.
 
     dtype "fp8": per-tensor quantization (scales stay on the device and are
     read by the kernel, so no host synchronisation); with ``fold_q`` the query
     takes the folded scale (see attn_quantize_fp8). With ``hadamard`` (fp8
     only; implies ``fold_q``) Q and K are rotated before the cast.
-    "bf16": RNE cast.
+    "bf16": RNE cast. ``flags`` (ATTN_FLAG_* bits) go to the attention call.
     Returns (o, lse, extras) where extras holds the codes and the scale tensor.
     """
     if hadamard and dtype != "fp8":
         raise ValueError("the Hadamard rotation applies to the fp8 path")
     if dtype == "fp8" and fold_q and not hadamard:
         (q8, k8, v8), scales = attn_quantize_fp8_qkv(q32, k32, v32, 1.0 / math.sqrt(q32.shape[-1]), stream=stream)
-        o, lse = attn_prefill_fwd(q8, k8, v8, causal=causal, d_scales=scales, stream=stream)
+        o, lse = attn_prefill_fwd(q8, k8, v8, causal=causal, d_scales=scales, stream=stream, flags=flags)
         return o, lse, dict(q=q8, k=k8, v=v8, scales=scales)
     if dtype == "fp8":
         scales = torch.empty(3, dtype=torch.float32, device=q32.device)
@@ -375,10 +377,10 @@ def prefill(q32: torch.Tensor, k32: torch.Tensor, v32: torch.Tensor, dtype: str 
                                       softmax_scale=1.0 / math.sqrt(q32.shape[-1]))
         else:
             q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream)
-        o, lse = attn_prefill_fwd(q8, k8, v8, causal=causal, d_scales=scales, stream=stream)
+        o, lse = attn_prefill_fwd(q8, k8, v8, causal=causal, d_scales=scales, stream=stream, flags=flags)
         return o, lse, dict(q=q8, k=k8, v=v8, scales=scales)
     if dtype == "bf16":
         qb, kb, vb = (attn_cast_bf16(t, stream=stream) for t in (q32, k32, v32))
-        o, lse = attn_prefill_fwd(qb, kb, vb, causal=causal, stream=stream)
+        o, lse = attn_prefill_fwd(qb, kb, vb, causal=causal, stream=stream, flags=flags)
         return o, lse, dict(q=qb, k=kb, v=vb, scales=None)
     raise ValueError("dtype must be 'fp8' or 'bf16'")

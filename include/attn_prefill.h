@@ -79,19 +79,35 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
                      int B, int S, int Hq, int Hkv, int d_qk, int d_v,
                      int causal, int dtype, hipStream_t stream);
 
+enum {
+  /*
+   * FP8 only: per (query row, 64-key block) power-of-two scaling of P. Each
+   * block's probabilities are rounded to e4m3 as p * 2^k (k >= 0, one k per
+   * row and block) and the P.V MFMA multiplies its products by 2^-k again
+   * through the power-of-two (E8M0) scale of its P operand, so small
+   * probabilities keep normal e4m3 precision (aicronaca.it, "Perché l'FP8
+   * non basta da solo"; ai4bro.com, "How does ZYFA work?"). O is still
+   * divided by the fp32 sum of the exact exponentials and LSE is unchanged.
+   */
+  ATTN_FLAG_P_BLOCK_SCALE = 1,
+};
+
 /*
- * As attn_prefill_fwd, with an explicit softmax scale (> 0, finite) and the
+ * As attn_prefill_fwd, with an explicit softmax scale (> 0, finite), the
  * three dequantization scales read from DEVICE memory (each a pointer to one
  * float, e.g. the output of attn_quantize_fp8), so a quantize -> attention
- * sequence needs no host synchronisation. Passing d_scales == NULL uses
- * q_scale, k_scale, v_scale from the host arguments instead.
+ * sequence needs no host synchronisation, and option flags. Passing
+ * d_scales == NULL uses q_scale, k_scale, v_scale from the host arguments
+ * instead.
  *   d_scales    NULL, or device float[3] = {q_scale, k_scale, v_scale}.
+ *   flags       0 or ATTN_FLAG_* bits: an unknown bit is ATTN_ERR_INVALID, a
+ *               flag with dtype BF16 ATTN_ERR_UNSUPPORTED.
  */
 int attn_prefill_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                         float q_scale, float k_scale, float v_scale, const float* d_scales,
                         float softmax_scale,
                         int B, int S, int Hq, int Hkv, int d_qk, int d_v,
-                        int causal, int dtype, hipStream_t stream);
+                        int causal, int dtype, int flags, hipStream_t stream);
 
 /*
  * Per-tensor FP8 quantize-and-layout step (the input side of the FP8 path).
@@ -190,7 +206,7 @@ int attn_cast_bf16(const float* x, uint16_t* y, int64_t n, hipStream_t stream);
 const char* attn_strerror(int code);
 
 /* ABI version of this header: 2 (2: quantizers take (x, x_dtype, x8, d_scale, n, ...),
- * the cast (x, y, n, ...)). */
+ * the cast (x, y, n, ...), attn_prefill_fwd_ex takes flags). */
 int attn_abi_version(void);
 
 #ifdef __cplusplus

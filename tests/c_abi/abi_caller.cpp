@@ -135,17 +135,29 @@ int main() {
   ATTN_OK_(attn_quantize_fp8(dk, 0, k8, dscales + 1, (int64_t)nkv, st));
   ATTN_OK_(attn_quantize_fp8(dv, 0, v8, dscales + 2, (int64_t)nkv, st));
   ATTN_OK_(attn_quantize_fp8_q(dq, 0, q8, dscales, (int64_t)nq, dscales + 1, sm, st));
-  ATTN_OK_(attn_prefill_fwd_ex(q8, k8, v8, dout, dlse, 1.f, 1.f, 1.f, dscales, sm, B, S, HQ, HKV, D, D, 1,
-                               ATTN_DTYPE_FP8_E4M3, st));
+  // (a flag outside the ABI, or a flag on the BF16 path, is rejected on the host)
+  if (attn_prefill_fwd_ex(q8, k8, v8, dout, dlse, 1.f, 1.f, 1.f, dscales, sm, B, S, HQ, HKV, D, D, 1,
+                          ATTN_DTYPE_FP8_E4M3, 1 << 20, st) != ATTN_ERR_INVALID ||
+      attn_prefill_fwd_ex(qb, kb, vb, dout, dlse, 1.f, 1.f, 1.f, nullptr, sm, B, S, HQ, HKV, D, D, 1,
+                          ATTN_DTYPE_BF16, ATTN_FLAG_P_BLOCK_SCALE, st) != ATTN_ERR_UNSUPPORTED) {
+    fprintf(stderr, "bad flags were not rejected\n");
+    return 1;
+  }
   std::vector<uint8_t> hv8(nkv);
   float hs[3];
-  HIP_OK(hipMemcpyAsync(hv8.data(), v8, nkv, hipMemcpyDeviceToHost, st));
-  HIP_OK(hipMemcpyAsync(hs, dscales, 12, hipMemcpyDeviceToHost, st));
-  HIP_OK(hipMemcpyAsync(o.data(), dout, nq * 2, hipMemcpyDeviceToHost, st));
-  HIP_OK(hipMemcpyAsync(lse.data(), dlse, lse.size() * 4, hipMemcpyDeviceToHost, st));
-  HIP_OK(hipStreamSynchronize(st));
-  for (size_t i = 0; i < nkv; ++i) vdeq[i] = e4m3fn_value(hv8[i]) * hs[2];
-  if (check("fp8", o, lse, vdeq)) return 1;
+  // exact probabilities, then the block-scaled form (for Q = 0 every p is 1,
+  // exact under any power-of-two scaling)
+  for (int flags : {0, (int)ATTN_FLAG_P_BLOCK_SCALE}) {
+    ATTN_OK_(attn_prefill_fwd_ex(q8, k8, v8, dout, dlse, 1.f, 1.f, 1.f, dscales, sm, B, S, HQ, HKV, D, D, 1,
+                                 ATTN_DTYPE_FP8_E4M3, flags, st));
+    HIP_OK(hipMemcpyAsync(hv8.data(), v8, nkv, hipMemcpyDeviceToHost, st));
+    HIP_OK(hipMemcpyAsync(hs, dscales, 12, hipMemcpyDeviceToHost, st));
+    HIP_OK(hipMemcpyAsync(o.data(), dout, nq * 2, hipMemcpyDeviceToHost, st));
+    HIP_OK(hipMemcpyAsync(lse.data(), dlse, lse.size() * 4, hipMemcpyDeviceToHost, st));
+    HIP_OK(hipStreamSynchronize(st));
+    for (size_t i = 0; i < nkv; ++i) vdeq[i] = e4m3fn_value(hv8[i]) * hs[2];
+    if (check(flags ? "fp8 block-scaled P" : "fp8", o, lse, vdeq)) return 1;
+  }
 
   // ---- BF16: RNE casts, then the same closed form
   ATTN_OK_(attn_cast_bf16(dq, qb, (int64_t)nq, st));

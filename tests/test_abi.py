@@ -72,8 +72,16 @@ def test_fwd_ex_rejects_bad_softmax_scale_and_scale_pointer():
     L = ops.lib()
     f = L.attn_prefill_fwd_ex
     args = [FAKE, FAKE, FAKE, FAKE, None, 1.0, 1.0, 1.0, None]
-    assert f(*args, 0.0, 1, 64, 2, 2, 128, 128, 1, 0, None) == INVALID
-    assert f(*args[:8], FAKE + 2, 0.1, 1, 64, 2, 2, 128, 128, 1, 0, None) == INVALID
+    assert f(*args, 0.0, 1, 64, 2, 2, 128, 128, 1, 0, 0, None) == INVALID
+    assert f(*args[:8], FAKE + 2, 0.1, 1, 64, 2, 2, 128, 128, 1, 0, 0, None) == INVALID
+
+
+def test_fwd_ex_flags():
+    f = ops.lib().attn_prefill_fwd_ex
+    args = [FAKE, FAKE, FAKE, FAKE, None, 1.0, 1.0, 1.0, None, 0.1, 1, 64, 2, 2, 128, 128, 1]
+    assert f(*args, 0, 1 << 9, None) == INVALID                             # unknown flag
+    assert f(*args, 1, ops.ATTN_FLAG_P_BLOCK_SCALE, None) == UNSUPPORTED    # BF16 has no scaled MFMA
+    assert f(*args[:4], FAKE + 2, *args[5:], 0, ops.ATTN_FLAG_P_BLOCK_SCALE, None) == INVALID  # misaligned lse
 
 
 def test_quantize_q_rejects_bad_arguments():
