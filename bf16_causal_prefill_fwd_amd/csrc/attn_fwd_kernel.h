@@ -237,7 +237,26 @@ enum ScoreForm { kScaleFma = 0, kScaleFolded = 1 };
 //    falling into the subnormal range (aicronaca.it, "Perché l'FP8 non basta
 //    da solo"; ai4bro.com, "How does ZYFA work?": power-of-two scaling of
 //    each 64-key block of P, absorbed by the scaled MFMA).
-enum PMode { kPExact = 0, kPBlockScaled = 1 };
+//  * kPLean (FP8, O only: no LSE): Lean P (Le Fil IA, context paragraph;
+//    aicronaca.it, "Perché l'FP8 non basta da solo"; ai4bro.com, "How does
+//    ZYFA work?"). An e4m3 code read as an integer grows by 8 per doubling
+//    of its value, so the code of p = 2^x is about 8x + 56 (1.0 is code 56,
+//    linear within each binade): the scores come out of the Q.K^T MFMA
+//    already as y = 8x + 56 + 8kb (the folded scale times 8, and a preset
+//    accumulator), and one conversion per score rounds y to an integer and
+//    clamps it to a byte, which is the e4m3 code fed to the P.V MFMA. No
+//    exp2 runs. kb is an integer shift per (query row, 64-key block), taken
+//    back by the P operand's E8M0 scale, that keeps every block's largest
+//    code in (96, 104]; O is divided by the sum of the same rounded
+//    probabilities, taken by one more MFMA (P times a block of ones).
+enum PMode { kPExact = 0, kPBlockScaled = 1, kPLean = 2 };
+
+// Lean P: a block's largest code is re-aimed into (kLeanTarget - 8,
+// kLeanTarget] when it leaves [kLeanLow, kLeanHigh] (code 127 is a NaN, 128
+// and up are negative); the shift stays within [-kMaxShift, kMaxShift]
+// after rebasing the O reference by 2^64 when it goes below -kLeanRebase.
+constexpr float kLeanTarget = 104.f, kLeanLow = 56.f, kLeanHigh = 126.f;
+constexpr int kLeanRebase = 60;
 
 // Largest block shift: 2^-kMaxShift stays a normal fp32 and 127 - kMaxShift
 // a valid E8M0 scale.
@@ -253,9 +272,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   constexpr bool FOLD = FORM == kScaleFolded;
   static_assert(!FOLD || C::FP8, "scale folding needs the scaled FP8 MFMA");
   constexpr bool PS = PM == kPBlockScaled;
-  static_assert(!PS || C::FP8, "block-scaled P needs the scaled FP8 MFMA");
+  constexpr bool LEAN = PM == kPLean;
+  static_assert(!(LEAN && FOLD), "Lean P forms its codes with one fma per score: the fma form");
+  static_assert(!(PS || LEAN) || C::FP8, "block-scaled and Lean P need the scaled FP8 MFMA");
   // scaled MFMAs are not matched by scheduling groups: fences order the jobs
-  constexpr bool FENCED = FOLD || PS;
+  constexpr bool FENCED = FOLD || PS || LEAN;
 
   constexpr int BN = C::BN, DV = C::DV, NS = C::NSTAGE;
   const int tid = threadIdx.x;
@@ -448,6 +469,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // largest shift, where its zeros stay zeros.
   float kb_div = 1.f;
   int e8[2] = {127, 127};
+  // Lean P: the shift kb of the tile being converted, the code bias of the
+  // scores (56 + 8 (kb - m_ref), m_ref the integer reference of O, so the
+  // code of a score s is 8 c s + bias), and the row sum of the rounded
+  // probabilities (every register of lacc holds it).
+  int kb = 0;
+  float cbias = 0.f;
+  f32x16 lacc = f32x16{};
+  // e4m3 1.0 in every byte: the ones operand of the row-sum MFMA
+  const i32x8 ones8 = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                       0x38383838, 0x38383838, 0x38383838, 0x38383838};
   auto set_shift = [&](float lg) {
     if constexpr (PS) kb_div = pow2i((int)__builtin_amdgcn_fmed3f(floorf(lg) - 7.f, (float)-kMaxShift, 0.f));
   };
@@ -515,7 +546,10 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       const int tv = j % C::NOT, u = j / C::NOT;
       if constexpr (C::FP8) {
         i32x8 pop = {pv[0][0], pv[0][1], pv[0][2], pv[0][3], pv[1][0], pv[1][1], pv[1][2], pv[1][3]};
-        oacc[tv] = PS ? mfma_f8_scaled(a, pop, oacc[tv], 127, e8[PP]) : mfma_f8(a, pop, oacc[tv]);
+        oacc[tv] = (PS || LEAN) ? mfma_f8_scaled(a, pop, oacc[tv], 127, e8[PP]) : mfma_f8(a, pop, oacc[tv]);
+        if constexpr (LEAN) {
+          if (j == 0) lacc = mfma_f8_scaled(ones8, pop, lacc, 127, e8[PP]);
+        }
       } else {
         oacc[tv] = mfma_bf16(__builtin_bit_cast(bf16x8, a), pv[u], oacc[tv]);
       }
@@ -587,6 +621,20 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       pout[u][e + 3] = (__bf16)p3;
     }
   };
+  // Lean P chunk c: four scores to four codes (the code-unit score by one
+  // fma, then round to nearest even and clamp to [0, 255]; -inf, a hidden
+  // key, gives 0), packed into dword c & 3 of the score tile's P operand
+  const float c8 = 8.f * c_log2;
+  auto lean_chunk = [&](int c, auto Pc) {
+    constexpr int P = decltype(Pc)::value;
+    const f32x16* sc = sbuf[P];
+    PVec* pout = pbuf[P];
+    const int t = c >> 2, r = 4 * (c & 3);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_fmaf(sc[t][r + i], c8, cbias), i, w);
+    pout[t][c & 3] = pin((int)w);
+  };
   auto probs_chunk = [&](int c, auto Pc, float m, float& lsum, auto SHIFTc) {
     float pe[4];
     chunk_exp(c, Pc, m, SHIFTc, pe);
@@ -604,9 +652,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     const f32x16* sc = sbuf[P];
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < C::NST; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[t][r], sc[t][r + 1]));
+    for (int t = 0; t < C::NST; ++t) mx = max16(sc[t], mx);
     mx = fmaxf(mx, swap_halves(mx));
     // (block-scaled P: the block's largest probability after the update is
     // 2^lg, lg <= 0)
@@ -673,13 +719,37 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
         }
       }
     }
+    // Lean P: the block's largest code, from its largest score; the lanes
+    // whose block left the band (all on the first tile) re-aim it by a
+    // whole number of binades, which moves the code bias of this tile and
+    // the ones after it, and kb (on the first tile the shift instead sets
+    // the reference of O). Branch-free: the bias enters every code through
+    // the fma that forms it.
+    if constexpr (LEAN) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < C::NST; ++t) mx = max16(sbuf[P][t], mx);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float ymax = __builtin_fmaf(mx, c8, cbias);
+      const bool off = ymax > -1e30f && (FIRST || !(ymax >= kLeanLow && ymax <= kLeanHigh));
+      int dlt = (int)floorf((kLeanTarget - (off ? ymax : kLeanTarget)) * 0.125f);
+      if (!FIRST) dlt = min(dlt, kMaxShift - kb);
+      cbias += 8.f * (float)dlt;
+      if (!FIRST) kb += dlt;
+      // scores far above the reference: rebase O by 2^-64 (exact)
+      if (wave_any(kb < -kLeanRebase)) {
+        const float f = kb < -kLeanRebase ? 0x1p-64f : 1.f;
+#pragma unroll
+        for (int t = 0; t < C::NOT; ++t) oacc[t] *= f;
+        lacc *= f;
+        kb += kb < -kLeanRebase ? 64 : 0;
+      }
+    }
     // block-scaled P: the shift of tile n from its largest score
     if constexpr (PS) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < C::NST; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sbuf[P][t][r], sbuf[P][t][r + 1]));
+      for (int t = 0; t < C::NST; ++t) mx = max16(sbuf[P][t], mx);
       mx = fmaxf(mx, swap_halves(mx));
       set_shift(FOLD ? mx : mx * c_log2 - m_run);
     }
@@ -704,7 +774,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     // CHUNK_PIPE: the exponentials of chunk c + 1 go out with the use of
     // chunk c, so no pack or add waits on a just-issued exp2
     float pe[2][4];
-    if (C::CHUNK_PIPE) chunk_exp(0, Pc{}, m_run, False_{}, pe[0]);
+    if (C::CHUNK_PIPE && !LEAN) chunk_exp(0, Pc{}, m_run, False_{}, pe[0]);
 #pragma unroll
     for (int j = 0; j < NJOB; ++j) {
       if (j + LA < NJOB) fr[(j + LA) % (LA + 1)] = load_frag(job_at(j + LA), vl, kl);
@@ -713,7 +783,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       // reads, and the last MFMA runs on while the wave waits at the barrier
       const int c_end = (j + 1) * NCHUNK / NJOB;
       for (; c < c_end; ++c) {
-        if (C::CHUNK_PIPE) {
+        if constexpr (LEAN) {
+          lean_chunk(c, Pc{});
+        } else if (C::CHUNK_PIPE) {
           if (c + 1 < NCHUNK) chunk_exp(c + 1, Pc{}, m_run, False_{}, pe[(c + 1) & 1]);
           chunk_use(c, Pc{}, pe[c & 1], lsum);
         } else {
@@ -743,10 +815,14 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
     __syncthreads();
     // lazy-max check of tile n after the barrier, by when its row sums are
     // complete (the exact path touches registers only)
-    const bool first = FOLD && FIRST;
-    if (wave_any(first | !(lsum <= kLazyMaxThreshold))) exact_path(Pc{}, lsum, first);
-    l_run += lsum;
-    if constexpr (PS) e8[P] = __float_as_int(kb_div) >> 23;  // 127 - kb, for tile n's P.V in step n + 1
+    if constexpr (LEAN) {
+      e8[P] = 127 - kb;  // for tile n's P.V in step n + 1
+    } else {
+      const bool first = FOLD && FIRST;
+      if (wave_any(first | !(lsum <= kLazyMaxThreshold))) exact_path(Pc{}, lsum, first);
+      l_run += lsum;
+      if constexpr (PS) e8[P] = __float_as_int(kb_div) >> 23;  // 127 - kb, for tile n's P.V in step n + 1
+    }
   };
 
   // ---- prologue: stages of K(0..NS-1) and V(0..NS-3) in flight, then all
@@ -826,7 +902,8 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   wait_vmcnt<0>();  // drain the loads of the last steps before the workgroup ends
 
   // ---- epilogue: O = O_acc * v_scale / l, LSE = ln2 * (m + log2 l)
-  const float l_tot = l_run + swap_halves(l_run);
+  // (Lean P: the rounded probabilities' row sum, over both key halves)
+  const float l_tot = LEAN ? lacc[0] : l_run + swap_halves(l_run);
   const float inv = vs / l_tot;
   if (qrow < S) {
     uint16_t* op = p.o + (((int64_t)b * S + qrow) * p.Hq + h) * DV;
@@ -845,7 +922,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
         *(uint2*)(op + dv) = make_uint2(w0, w1);
       }
     }
-    if (p.lse && g == 0) {
+    if (!LEAN && p.lse && g == 0) {
       p.lse[((int64_t)b * p.Hq + h) * S + qrow] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
     }
   }
@@ -863,7 +940,7 @@ __global__ __launch_bounds__(C::NTHREADS, C::WG_PER_CU) void attn_fwd_kernel(Fwd
   }
   // scores in log2 units: t = c * (q . k)
   const float c_log2 = qs * ks * p.sm_scale * 1.4426950408889634f;
-  if constexpr (C::FOLDABLE) {
+  if constexpr (C::FOLDABLE && PM != kPLean) {
     // c = f * 2^e, f in [0.5, 1): a power of two up to fp32 rounding of the
     // scale product (a relative 2^-18 covers it many times over)
     int e;

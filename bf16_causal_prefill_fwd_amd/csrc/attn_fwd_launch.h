@@ -26,12 +26,14 @@ inline LaunchStatus launch_fwd(FwdParams prm, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? kLaunched : kLaunchFailed;
 }
 
-// d_qk is 128 or 192 (d_v 128), and pmode kPExact for BF16, checked by the
-// caller.
+// d_qk is 128 or 192 (d_v 128), pmode kPExact for BF16 and lse null for
+// kPLean, checked by the caller.
 inline LaunchStatus launch_attn_fwd(FwdParams prm, bool fp8, int d_qk, int pmode, hipStream_t stream) {
   if (fp8 && pmode == kPBlockScaled)
     return d_qk == 128 ? launch_fwd<CfgF8D128, kPBlockScaled>(prm, stream)
                        : launch_fwd<CfgF8D192, kPBlockScaled>(prm, stream);
+  if (fp8 && pmode == kPLean)
+    return d_qk == 128 ? launch_fwd<CfgF8D128, kPLean>(prm, stream) : launch_fwd<CfgF8D192, kPLean>(prm, stream);
   if (fp8)
     return d_qk == 128 ? launch_fwd<CfgF8D128, kPExact>(prm, stream) : launch_fwd<CfgF8D192, kPExact>(prm, stream);
   return d_qk == 128 ? launch_fwd<CfgBFD128, kPExact>(prm, stream) : launch_fwd<CfgBFD192, kPExact>(prm, stream);

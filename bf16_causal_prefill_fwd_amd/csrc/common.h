@@ -61,6 +61,16 @@ __device__ __forceinline__ void lds_write_b128(ATTN_LDS char* p, const i32x4& v)
   *(ATTN_LDS i32x4*)p = v;
 }
 
+// Largest of 16 accumulator values and m (IEEE 754-2019 maximum: a NaN
+// would propagate; the values here are finite or -inf). This form compiles
+// to three-input v_maximum3_f32; fmaxf's NaN rules keep the compiler from
+// merging pairs of maxima of MFMA results.
+__device__ __forceinline__ float max16(const f32x16& x, float m) {
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) m = __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(x[r], x[r + 1]));
+  return m;
+}
+
 // Value of the other half-wave's lane (l ^ 32).
 __device__ __forceinline__ float swap_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);

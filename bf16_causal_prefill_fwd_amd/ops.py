@@ -21,6 +21,7 @@ ATTN_OK = 0
 ATTN_DTYPE_FP8_E4M3 = 0
 ATTN_DTYPE_BF16 = 1
 ATTN_FLAG_P_BLOCK_SCALE = 1
+ATTN_FLAG_LEAN_P = 2
 
 _lib = None
 
@@ -323,6 +324,10 @@ def attn_prefill_fwd(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True
     B, S, Hq, Hkv, dqk, dv, dt = check_attention_args(q, k, v, out, lse, d_scales)
     _need_current(q, "q")
     out = torch.empty((B, S, Hq, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
+    if flags & ATTN_FLAG_LEAN_P:
+        if lse is not None:
+            raise ValueError("Lean P computes O only: pass lse=None")
+        return_lse = False
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     L = lib()

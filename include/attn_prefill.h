@@ -90,6 +90,22 @@ enum {
    * divided by the fp32 sum of the exact exponentials and LSE is unchanged.
    */
   ATTN_FLAG_P_BLOCK_SCALE = 1,
+  /*
+   * FP8 only, O only (lse must be NULL; not with ATTN_FLAG_P_BLOCK_SCALE):
+   * Lean P (Le Fil IA, context paragraph; aicronaca.it, "Perché l'FP8 non
+   * basta da solo"; ai4bro.com, "How does ZYFA work?"). No exponential is
+   * evaluated: an e4m3 code read as an integer grows by 8 per doubling, so
+   * the code of p = 2^x is taken as round(8x + 56) (exact at powers of two,
+   * linear in between, up to 6.2% high), with a power-of-two shift per
+   * (query row, 64-key block) taken back by the P operand's E8M0 scale, and
+   * O is divided by the sum of these rounded probabilities (one more MFMA).
+   * An approximation: its O error is about 1.5 times that of the exact path.
+   * SWITCHED OFF: it misses the FP8 O bar of 3e-2 on part of the workloads
+   * and runs no faster than the exact path on this hardware, so every call
+   * with this flag (and no other argument error) returns
+   * ATTN_ERR_UNSUPPORTED.
+   */
+  ATTN_FLAG_LEAN_P = 2,
 };
 
 /*

@@ -82,6 +82,10 @@ def test_fwd_ex_flags():
     assert f(*args, 0, 1 << 9, None) == INVALID                             # unknown flag
     assert f(*args, 1, ops.ATTN_FLAG_P_BLOCK_SCALE, None) == UNSUPPORTED    # BF16 has no scaled MFMA
     assert f(*args[:4], FAKE + 2, *args[5:], 0, ops.ATTN_FLAG_P_BLOCK_SCALE, None) == INVALID  # misaligned lse
+    # Lean P: O only (an lse pointer is invalid), not with block scaling, and switched off
+    assert f(*args[:4], FAKE, *args[5:], 0, ops.ATTN_FLAG_LEAN_P, None) == INVALID
+    assert f(*args, 0, ops.ATTN_FLAG_LEAN_P | ops.ATTN_FLAG_P_BLOCK_SCALE, None) == INVALID
+    assert f(*args, 0, ops.ATTN_FLAG_LEAN_P, None) == UNSUPPORTED
 
 
 def test_quantize_q_rejects_bad_arguments():
