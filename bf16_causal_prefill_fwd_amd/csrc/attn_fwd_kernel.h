@@ -59,7 +59,7 @@ struct FwdParams {
   int xcd_remap;
 };
 
-template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_, bool STAGE_UNROLL_ = true>
+template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_, bool STAGE_UNROLL_ = true, int LOOKAHEAD_ = 2>
 struct FwdCfg {
   static constexpr bool FP8 = FP8_;
   static constexpr int DQK = DQK_, DV = DV_, BN = BN_;
@@ -79,12 +79,12 @@ struct FwdCfg {
   static constexpr int NSTAGE = NSTAGE_;             // K ring and V ring depth
   // main loop unrolled by NSTAGE (every ring stage a constant LDS offset, no
   // per-step address arithmetic) rather than by 2 (the score parity only);
-  // the longer loop body needs more registers, so a configuration that
-  // would spill keeps the short one
+  // the longer loop body needs more registers (every configuration built
+  // here takes the long one; the FP8 d_qk = 192 one with a look-ahead of 1)
   static constexpr bool STAGE_UNROLL = STAGE_UNROLL_;
-  static constexpr int LOOKAHEAD = 2;               // MFMA jobs whose LDS operand reads are in flight
+  static constexpr int LOOKAHEAD = LOOKAHEAD_;      // MFMA jobs whose LDS operand reads are in flight
   // softmax chunks software-pipelined (exponentials one chunk ahead of their
-  // use); measured 0.3% slower on the two-step-loop FP8 d_qk = 192 kernel
+  // use); measured 0.3% slower on a two-step loop
   static constexpr bool CHUNK_PIPE = STAGE_UNROLL;
   // folded score form available (the scaled MFMA exists for FP8 only)
   static constexpr bool FOLDABLE = FP8;

@@ -7,7 +7,10 @@
 namespace attn {
 
 using CfgF8D128 = FwdCfg<true, 128, 128, 64, 4>;
-using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4, false>;  // the NSTAGE-unrolled loop spills here
+// (FP8 d_qk = 192: the loop unrolled by the ring depth fits the 256
+// registers of two waves per SIMD only with one MFMA job's operand reads in
+// flight instead of two)
+using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4, true, 1>;
 using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4>;
 using CfgBFD192 = FwdCfg<false, 192, 128, 32, 4>;
 
