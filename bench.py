@@ -257,7 +257,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--hadamard", action="store_true",
-                    help="FP8: rotate Q and K by Hadamard blocks in the input step (attn_quantize_fp8_hadamard)")
+                    help="FP8: rotate Q and K by Hadamard blocks in the input step (attn_quantize_fp8_qkv_hadamard)")
     ap.add_argument("--p-block-scale", action="store_true",
                     help="FP8: per (row, 64-key block) power-of-two scaling of P (ATTN_FLAG_P_BLOCK_SCALE)")
     ap.add_argument("--seq-len", type=int, default=None, help="override the workload's sequence length")
@@ -329,15 +329,9 @@ def main(argv=None) -> int:
     flags = ops.ATTN_FLAG_P_BLOCK_SCALE if args.p_block_scale else 0
 
     def input_step():
-        if w.dtype == "fp8" and not args.hadamard:
-            ops.attn_quantize_fp8_qkv(q32, k32, v32, sm_scale, out=codes, scales=scales, stream=stream)
-        elif w.dtype == "fp8":
-            # K and V first: the query's folded scale is derived from K's
-            for i in (1, 2):
-                ops.attn_quantize_fp8((q32, k32, v32)[i], out=codes[i], scale=scales[i:i + 1], stream=stream,
-                                      hadamard=args.hadamard and i == 1)
-            ops.attn_quantize_fp8(q32, out=codes[0], scale=scales[0:1], stream=stream, k_scale=scales[1:2],
-                                  softmax_scale=sm_scale, hadamard=args.hadamard)
+        if w.dtype == "fp8":
+            ops.attn_quantize_fp8_qkv(q32, k32, v32, sm_scale, out=codes, scales=scales, stream=stream,
+                                      hadamard=args.hadamard)
         else:
             for i, t in enumerate((q32, k32, v32)):
                 ops.attn_cast_bf16(t, out=codes[i], stream=stream)

@@ -155,12 +155,13 @@ int attn_quantize_fp8_q(const void* x, int x_dtype, uint8_t* x8, float* d_scale,
   return quantize_impl(x, x_dtype, n, x8, d_scale, d_k_scale, softmax_scale, 0, stream);
 }
 
-int attn_quantize_fp8_qkv(const void* q, const void* k, const void* v, int x_dtype, int64_t nq, int64_t nk,
-                          int64_t nv, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* d_scales, float softmax_scale,
-                          hipStream_t stream) {
-  const void* x[3] = {q, k, v};
-  const int64_t n[3] = {nq, nk, nv};
-  uint8_t* const x8[3] = {q8, k8, v8};
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two fused Q/K/V input steps.
+int qkv_check(const void* const x[3], int x_dtype, const int64_t n[3], uint8_t* const x8[3], const float* d_scales,
+              float softmax_scale) {
   if (!d_scales || ((uintptr_t)d_scales & 3u)) return ATTN_ERR_INVALID;
   if (!(isfinite(softmax_scale) && softmax_scale > 0.f)) return ATTN_ERR_INVALID;
   if (x_dtype != 0 && x_dtype != 1) return ATTN_ERR_UNSUPPORTED;
@@ -174,9 +175,43 @@ int attn_quantize_fp8_qkv(const void* q, const void* k, const void* v, int x_dty
     const char* ob = (const char*)x8[i];
     if ((sb + 12 > xb && sb < xe) || (sb + 12 > ob && sb < ob + n[i])) return ATTN_ERR_INVALID;
   }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_quantize_fp8_qkv(const void* q, const void* k, const void* v, int x_dtype, int64_t nq, int64_t nk,
+                          int64_t nv, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* d_scales, float softmax_scale,
+                          hipStream_t stream) {
+  const void* x[3] = {q, k, v};
+  const int64_t n[3] = {nq, nk, nv};
+  uint8_t* const x8[3] = {q8, k8, v8};
+  const int bad = qkv_check(x, x_dtype, n, x8, d_scales, softmax_scale);
+  if (bad != ATTN_OK) return bad;
   const int ready = attn::device_ready();
   if (ready != ATTN_OK) return ready;
   return attn::launch_quantize_fp8_qkv(x, x_dtype, n, x8, d_scales, softmax_scale, stream) == hipSuccess
+             ? ATTN_OK
+             : ATTN_ERR_HIP;
+}
+
+int attn_quantize_fp8_qkv_hadamard(const void* q, const void* k, const void* v, int x_dtype, int64_t nq, int64_t nk,
+                                   int64_t nv, int d, uint8_t* q8, uint8_t* k8, uint8_t* v8, float* d_scales,
+                                   float softmax_scale, hipStream_t stream) {
+  const void* x[3] = {q, k, v};
+  const int64_t n[3] = {nq, nk, nv};
+  uint8_t* const x8[3] = {q8, k8, v8};
+  const int bad = qkv_check(x, x_dtype, n, x8, d_scales, softmax_scale);
+  if (bad != ATTN_OK) return bad;
+  if (d <= 0 || nq % d != 0 || nk % d != 0) return ATTN_ERR_INVALID;
+  const int block = (d & -d) < 128 ? (d & -d) : 128;
+  if (block != 64 && block != 128) return ATTN_ERR_UNSUPPORTED;
+  const int ready = attn::device_ready();
+  if (ready != ATTN_OK) return ready;
+  return attn::launch_quantize_fp8_qkv_hadamard(x, x_dtype, n, block, x8, d_scales, softmax_scale, stream) ==
+                 hipSuccess
              ? ATTN_OK
              : ATTN_ERR_HIP;
 }

@@ -220,9 +220,10 @@ __global__ __launch_bounds__(QTHREADS) void quant3_kernel(Qkv3 a) {
   quant_body<XDT>(a.x[i], a.n[i], scale, a.out[i], blockIdx.x - a.first[i], a.nblk[i]);
 }
 
-__global__ void scale3_finalize_kernel(uint32_t* bits, float sm_scale) {
+// (q_post: 1, or 1/b for a rotated query: exact, b is a power of two)
+__global__ void scale3_finalize_kernel(uint32_t* bits, float sm_scale, float q_post) {
   const float ks = scale_from_amax(bits[1]), vs = scale_from_amax(bits[2]);
-  const float qs = folded_scale_from_amax(bits[0], ks, sm_scale);
+  const float qs = folded_scale_from_amax(bits[0], ks, sm_scale) * q_post;
   bits[0] = __float_as_uint(qs);
   bits[1] = __float_as_uint(ks);
   bits[2] = __float_as_uint(vs);
@@ -318,13 +319,14 @@ __device__ __forceinline__ void had_rotate(const void* __restrict__ x, int64_t b
 }
 
 // Each wave takes 16 block rows per trip; the trip count is uniform per wave.
+// The bodies serve the workgroups blk = 0 .. nblk-1 assigned to the tensor.
 template <int XDT, int BLK>
-__global__ __launch_bounds__(QTHREADS) void had_amax_kernel(const void* __restrict__ x, int64_t nbr,
-                                                             uint32_t* amax_bits) {
+__device__ __forceinline__ void had_amax_body(const void* __restrict__ x, int64_t nbr, uint32_t* amax_bits, int blk,
+                                              int nblk) {
   using H = HadShape<XDT, BLK>;
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (QTHREADS / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (QTHREADS / 64);
+  const int64_t wave = (int64_t)blk * (QTHREADS / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)nblk * (QTHREADS / 64);
   float m = 0.f;
   for (int64_t br0 = wave * 16; br0 < nbr; br0 += nwaves * 16) {
     double y[H::NE];
@@ -346,15 +348,19 @@ __global__ __launch_bounds__(QTHREADS) void had_amax_kernel(const void* __restri
 }
 
 template <int XDT, int BLK>
-__global__ __launch_bounds__(QTHREADS) void had_quant_kernel(const void* __restrict__ x, int64_t nbr,
-                                                              const uint32_t* __restrict__ amax_bits,
-                                                              const float* __restrict__ d_k_scale, float sm_scale,
-                                                              uint8_t* __restrict__ out) {
+__global__ __launch_bounds__(QTHREADS) void had_amax_kernel(const void* __restrict__ x, int64_t nbr,
+                                                             uint32_t* amax_bits) {
+  had_amax_body<XDT, BLK>(x, nbr, amax_bits, blockIdx.x, gridDim.x);
+}
+
+template <int XDT, int BLK>
+__device__ __forceinline__ void had_quant_body(const void* __restrict__ x, int64_t nbr, float scale,
+                                               uint8_t* __restrict__ out, int blk, int nblk) {
   using H = HadShape<XDT, BLK>;
-  const double rcp = 1.0 / (double)quant_scale(*amax_bits, d_k_scale, sm_scale);
+  const double rcp = 1.0 / (double)scale;
   const int lane = threadIdx.x & 63, j = lane & 3;
-  const int64_t wave = (int64_t)blockIdx.x * (QTHREADS / 64) + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (QTHREADS / 64);
+  const int64_t wave = (int64_t)blk * (QTHREADS / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)nblk * (QTHREADS / 64);
   for (int64_t br0 = wave * 16; br0 < nbr; br0 += nwaves * 16) {
     const int64_t br = br0 + (lane >> 2);
     double y[H::NE];
@@ -376,6 +382,39 @@ __global__ __launch_bounds__(QTHREADS) void had_quant_kernel(const void* __restr
       }
     }
   }
+}
+
+template <int XDT, int BLK>
+__global__ __launch_bounds__(QTHREADS) void had_quant_kernel(const void* __restrict__ x, int64_t nbr,
+                                                              const uint32_t* __restrict__ amax_bits,
+                                                              const float* __restrict__ d_k_scale, float sm_scale,
+                                                              uint8_t* __restrict__ out) {
+  had_quant_body<XDT, BLK>(x, nbr, quant_scale(*amax_bits, d_k_scale, sm_scale), out, blockIdx.x, gridDim.x);
+}
+
+// ---- the rotated input step of one attention call: Q and K rotated, V
+// plain, split over the workgroups of one absmax launch and one encode
+// launch as in Qkv3 (Q folded with the rotated K's scale; its stored scale
+// is then divided by the block size). The codes and scales are those of the
+// three separate calls.
+template <int XDT, int BLK>
+__global__ __launch_bounds__(QTHREADS) void had_amax3_kernel(Qkv3 a) {
+  const int i = qkv_range(a, blockIdx.x);
+  if (i < 2) had_amax_body<XDT, BLK>(a.x[i], a.n[i] / BLK, a.bits + i, blockIdx.x - a.first[i], a.nblk[i]);
+  else amax_body<XDT>(a.x[2], a.n[2], a.bits + 2, blockIdx.x - a.first[2], a.nblk[2]);
+}
+
+template <int XDT, int BLK>
+__global__ __launch_bounds__(QTHREADS) void had_quant3_kernel(Qkv3 a) {
+  const int i = qkv_range(a, blockIdx.x);
+  const float ks = scale_from_amax(a.bits[1]);
+  if (i == 0)
+    had_quant_body<XDT, BLK>(a.x[0], a.n[0] / BLK, folded_scale_from_amax(a.bits[0], ks, a.sm_scale), a.out[0],
+                             blockIdx.x - a.first[0], a.nblk[0]);
+  else if (i == 1)
+    had_quant_body<XDT, BLK>(a.x[1], a.n[1] / BLK, ks, a.out[1], blockIdx.x - a.first[1], a.nblk[1]);
+  else
+    quant_body<XDT>(a.x[2], a.n[2], scale_from_amax(a.bits[2]), a.out[2], blockIdx.x - a.first[2], a.nblk[2]);
 }
 
 // fp32 -> bf16, round to nearest even (finite inputs).
@@ -433,15 +472,14 @@ hipError_t launch_quantize_fp8(const void* x, int x_dtype, int64_t n, uint8_t* x
   return hipGetLastError();
 }
 
+static int had_grid(int64_t nbr);
+
 template <int XDT, int BLK>
 static void launch_had(const void* x, int64_t nbr, uint32_t* bits, const float* d_k_scale, float sm_scale,
                        uint8_t* x8, hipStream_t stream) {
-  // 64 block rows per workgroup trip (16 per wave), up to 16 workgroups per CU
-  int64_t g = (nbr + 63) / 64;
-  if (g > 256 * 16) g = 256 * 16;
-  if (g < 1) g = 1;
-  hipLaunchKernelGGL((had_amax_kernel<XDT, BLK>), dim3((int)g), dim3(QTHREADS), 0, stream, x, nbr, bits);
-  hipLaunchKernelGGL((had_quant_kernel<XDT, BLK>), dim3((int)g), dim3(QTHREADS), 0, stream, x, nbr, bits, d_k_scale,
+  const int g = had_grid(nbr);
+  hipLaunchKernelGGL((had_amax_kernel<XDT, BLK>), dim3(g), dim3(QTHREADS), 0, stream, x, nbr, bits);
+  hipLaunchKernelGGL((had_quant_kernel<XDT, BLK>), dim3(g), dim3(QTHREADS), 0, stream, x, nbr, bits, d_k_scale,
                      sm_scale, x8);
 }
 
@@ -485,7 +523,48 @@ hipError_t launch_quantize_fp8_qkv(const void* const x[3], int x_dtype, const in
     hipLaunchKernelGGL(amax3_kernel<1>, dim3(total), dim3(QTHREADS), 0, stream, a);
     hipLaunchKernelGGL(quant3_kernel<1>, dim3(total), dim3(QTHREADS), 0, stream, a);
   }
-  hipLaunchKernelGGL(scale3_finalize_kernel, dim3(1), dim3(1), 0, stream, a.bits, sm_scale);
+  hipLaunchKernelGGL(scale3_finalize_kernel, dim3(1), dim3(1), 0, stream, a.bits, sm_scale, 1.0f);
+  return hipGetLastError();
+}
+
+static int had_grid(int64_t nbr) {
+  // 64 block rows per workgroup trip (16 per wave), up to 16 workgroups per CU
+  int64_t g = (nbr + 63) / 64;
+  if (g > 256 * 16) g = 256 * 16;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+template <int XDT, int BLK>
+static void launch_had3(const Qkv3& a, int total, hipStream_t stream) {
+  hipLaunchKernelGGL((had_amax3_kernel<XDT, BLK>), dim3(total), dim3(QTHREADS), 0, stream, a);
+  hipLaunchKernelGGL((had_quant3_kernel<XDT, BLK>), dim3(total), dim3(QTHREADS), 0, stream, a);
+}
+
+hipError_t launch_quantize_fp8_qkv_hadamard(const void* const x[3], int x_dtype, const int64_t n[3], int block,
+                                            uint8_t* const x8[3], float* d_scales, float sm_scale,
+                                            hipStream_t stream) {
+  Qkv3 a{};
+  int total = 0;
+  for (int i = 0; i < 3; ++i) {
+    a.x[i] = x[i];
+    a.n[i] = n[i];
+    a.out[i] = x8[i];
+    a.first[i] = total;
+    a.nblk[i] = i < 2 ? had_grid(n[i] / block) : stream_grid(n[i]);
+    total += a.nblk[i];
+  }
+  a.bits = (uint32_t*)d_scales;
+  a.sm_scale = sm_scale;
+  hipLaunchKernelGGL(amax3_reset_kernel, dim3(1), dim3(64), 0, stream, a.bits);
+  if (block == 128) {
+    if (x_dtype == 0) launch_had3<0, 128>(a, total, stream);
+    else launch_had3<1, 128>(a, total, stream);
+  } else {
+    if (x_dtype == 0) launch_had3<0, 64>(a, total, stream);
+    else launch_had3<1, 64>(a, total, stream);
+  }
+  hipLaunchKernelGGL(scale3_finalize_kernel, dim3(1), dim3(1), 0, stream, a.bits, sm_scale, 1.0f / (float)block);
   return hipGetLastError();
 }
 

@@ -46,6 +46,9 @@ _SIGNATURES = {
                                             _c_float, _c_void_p]),
     "attn_quantize_fp8_qkv": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int64, _c_int64, _c_int64,
                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_float, _c_void_p]),
+    "attn_quantize_fp8_qkv_hadamard": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int64, _c_int64,
+                                                _c_int64, _c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                                _c_float, _c_void_p]),
     "attn_cast_bf16": (_c_int, [_c_void_p, _c_void_p, _c_int64, _c_void_p]),
     "attn_strerror": (ctypes.c_char_p, [_c_int]),
     "attn_abi_version": (_c_int, []),
@@ -228,20 +231,31 @@ def check_quantize_qkv_args(q, k, v, out=None, scales=None) -> int:
 
 
 def attn_quantize_fp8_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, softmax_scale: float,
-                          out=None, scales: torch.Tensor | None = None, stream=None):
+                          out=None, scales: torch.Tensor | None = None, stream=None, hadamard: bool = False):
     """The FP8 input step of one attention call in one pass per kind of work
     (attn_quantize_fp8_qkv): K and V with plain scales, Q with the folded one.
+    With ``hadamard`` Q and K are rotated first (attn_quantize_fp8_qkv_hadamard;
+    the head dim is the last axis of q and k).
     Returns ((q8, k8, v8) uint8 tensors shaped like the inputs, scales float32
     device tensor [3] = {q_scale, k_scale, v_scale})."""
     out = tuple(out) if out is not None else None
     xdt = check_quantize_qkv_args(q, k, v, out, scales)
+    if hadamard and (q.dim() < 1 or k.dim() < 1 or q.shape[-1] != k.shape[-1]):
+        raise ValueError("the rotation needs q and k with the same head dim (last axis)")
     _need_current(q, "q")
     out = tuple(torch.empty(t.shape, dtype=torch.uint8, device=t.device) for t in (q, k, v)) if out is None else out
     scales = torch.empty(3, dtype=torch.float32, device=q.device) if scales is None else scales
-    _check("attn_quantize_fp8_qkv",
-           lib().attn_quantize_fp8_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), xdt, q.numel(), k.numel(),
-                                       v.numel(), out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
-                                       scales.data_ptr(), float(softmax_scale), _stream(stream)))
+    if hadamard:
+        _check("attn_quantize_fp8_qkv_hadamard",
+               lib().attn_quantize_fp8_qkv_hadamard(q.data_ptr(), k.data_ptr(), v.data_ptr(), xdt, q.numel(),
+                                                    k.numel(), v.numel(), q.shape[-1], out[0].data_ptr(),
+                                                    out[1].data_ptr(), out[2].data_ptr(), scales.data_ptr(),
+                                                    float(softmax_scale), _stream(stream)))
+    else:
+        _check("attn_quantize_fp8_qkv",
+               lib().attn_quantize_fp8_qkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), xdt, q.numel(), k.numel(),
+                                           v.numel(), out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+                                           scales.data_ptr(), float(softmax_scale), _stream(stream)))
     return out, scales
 
 
@@ -366,22 +380,16 @@ def prefill(q32: torch.Tensor, k32: torch.Tensor, v32: torch.Tensor, dtype: str 
     """
     if hadamard and dtype != "fp8":
         raise ValueError("the Hadamard rotation applies to the fp8 path")
-    if dtype == "fp8" and fold_q and not hadamard:
-        (q8, k8, v8), scales = attn_quantize_fp8_qkv(q32, k32, v32, 1.0 / math.sqrt(q32.shape[-1]), stream=stream)
+    if dtype == "fp8" and (fold_q or hadamard):
+        (q8, k8, v8), scales = attn_quantize_fp8_qkv(q32, k32, v32, 1.0 / math.sqrt(q32.shape[-1]), stream=stream,
+                                                     hadamard=hadamard)
         o, lse = attn_prefill_fwd(q8, k8, v8, causal=causal, d_scales=scales, stream=stream, flags=flags)
         return o, lse, dict(q=q8, k=k8, v=v8, scales=scales)
     if dtype == "fp8":
         scales = torch.empty(3, dtype=torch.float32, device=q32.device)
-        k8, _ = attn_quantize_fp8(k32, scale=scales[1:2], stream=stream, hadamard=hadamard)
+        k8, _ = attn_quantize_fp8(k32, scale=scales[1:2], stream=stream)
         v8, _ = attn_quantize_fp8(v32, scale=scales[2:3], stream=stream)
-        if hadamard:
-            q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream, k_scale=scales[1:2],
-                                      softmax_scale=1.0 / math.sqrt(q32.shape[-1]), hadamard=True)
-        elif fold_q:
-            q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream, k_scale=scales[1:2],
-                                      softmax_scale=1.0 / math.sqrt(q32.shape[-1]))
-        else:
-            q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream)
+        q8, _ = attn_quantize_fp8(q32, scale=scales[0:1], stream=stream)
         o, lse = attn_prefill_fwd(q8, k8, v8, causal=causal, d_scales=scales, stream=stream, flags=flags)
         return o, lse, dict(q=q8, k=k8, v=v8, scales=scales)
     if dtype == "bf16":

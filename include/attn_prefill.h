@@ -211,6 +211,22 @@ int attn_quantize_fp8_hadamard(const void* x, int x_dtype, uint8_t* x8, float* d
                                const float* d_k_scale, float softmax_scale, hipStream_t stream);
 
 /*
+ * The rotated FP8 input step of one attention call: Q and K rotated by
+ * Hadamard blocks as in attn_quantize_fp8_hadamard (Q with the folded scale
+ * for the rotated K's scale, its stored scale divided by the block size), V
+ * plain, in one absmax launch and one encode launch over the three tensors
+ * (aicronaca.it, "Perché l'FP8 non basta da solo": the rotation costs a
+ * small fraction of the attention time). Arguments as attn_quantize_fp8_qkv,
+ * plus d, the head dim of Q and K (nq and nk multiples of it; blocks of
+ * 64 or 128 columns as attn_quantize_fp8_hadamard, else
+ * ATTN_ERR_UNSUPPORTED). The codes and scales equal those of the three
+ * separate calls.
+ */
+int attn_quantize_fp8_qkv_hadamard(const void* q, const void* k, const void* v, int x_dtype, int64_t nq,
+                                   int64_t nk, int64_t nv, int d, uint8_t* q8, uint8_t* k8, uint8_t* v8,
+                                   float* d_scales, float softmax_scale, hipStream_t stream);
+
+/*
  * BF16 input step: float32 -> bfloat16, round to nearest, ties to even (the
  * BF16 path takes its inputs unquantized: Le Fil IA, summary paragraph).
  *   x  device float32[n];  y  device bfloat16[n] (as uint16 bits), both

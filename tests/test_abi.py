@@ -23,8 +23,8 @@ FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced by host
 def test_exports_every_header_function():
     names = ops.header_functions()
     assert set(names) == {"attn_prefill_fwd", "attn_prefill_fwd_ex", "attn_quantize_fp8", "attn_quantize_fp8_q",
-                          "attn_quantize_fp8_hadamard", "attn_quantize_fp8_qkv", "attn_cast_bf16", "attn_strerror",
-                          "attn_abi_version"}
+                          "attn_quantize_fp8_hadamard", "attn_quantize_fp8_qkv", "attn_quantize_fp8_qkv_hadamard",
+                          "attn_cast_bf16", "attn_strerror", "attn_abi_version"}
     L = ctypes.CDLL(build_mod.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -153,6 +153,28 @@ def test_quantize_qkv_rejects_bad_arguments():
     assert call(sc=sc + 2) == INVALID          # misaligned scales
     assert call(sc=v + 1020) == INVALID        # scales overlap the end of v
     assert call(sc=k8 + 16) == INVALID         # scales inside k's codes
+
+
+def test_quantize_qkv_hadamard_rejects_bad_arguments():
+    f = ops.lib().attn_quantize_fp8_qkv_hadamard
+    q, k, v = FAKE, FAKE + 1024, FAKE + 2048
+    q8, k8, v8, sc = FAKE + 4096, FAKE + 4352, FAKE + 4608, FAKE + 8192
+    names = ["q", "k", "v", "xdt", "nq", "nk", "nv", "d", "q8", "k8", "v8", "sc", "sm", "st"]
+    ok = (q, k, v, 0, 256, 256, 256, 128, q8, k8, v8, sc, 0.1, None)
+
+    def call(**kw):
+        a = list(ok)
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+    assert call(q=None) == INVALID
+    assert call(sc=sc + 2) == INVALID
+    assert call(sm=0.0) == INVALID
+    assert call(d=0) == INVALID
+    assert call(d=96) == INVALID                # 256 is not a multiple of 96
+    assert call(d=32) == UNSUPPORTED            # 32-column blocks
+    assert call(nk=200) == INVALID              # k not whole rows
+    assert call(xdt=2) == UNSUPPORTED
 
 
 # ---------------------------------------------------------------- binding-side checks (no GPU)

@@ -160,3 +160,30 @@ def test_full_size_gqa_rotated():
     lerr = float(np.max(np.abs(lg - ref["lse_rows"])))
     print(f"  LSE max-abs {lerr:.3e}", flush=True)
     assert lerr <= LSE_TOL
+
+
+@pytest.mark.parametrize("xdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("dqk", [128, 192])
+def test_fused_rotated_input_step_matches_separate_calls(xdt, dqk):
+    # one absmax and one encode launch for rotated Q and K and plain V give
+    # the codes and scales of the three separate calls, and the oracle's
+    rng = np.random.default_rng(40 + dqk)
+    shapes = ((1, 333, 4, dqk), (1, 333, 2, dqk), (1, 333, 2, 128))
+    xs = []
+    for sh in shapes:
+        t, _ = _input(sh, xdt, int(rng.integers(1 << 30)))
+        xs.append(t)
+    print(f"case fused rotated input step {xdt} d_qk={dqk}", flush=True)
+    sm = 1.0 / math.sqrt(dqk)
+    (q8, k8, v8), sc = ops.attn_quantize_fp8_qkv(*xs, sm, hadamard=True)
+    k8s, ks = ops.attn_quantize_fp8(xs[1], hadamard=True)
+    v8s, vs = ops.attn_quantize_fp8(xs[2])
+    q8s, qs = ops.attn_quantize_fp8(xs[0], k_scale=ks, softmax_scale=sm, hadamard=True)
+    torch.cuda.synchronize()
+    assert torch.equal(q8, q8s) and torch.equal(k8, k8s) and torch.equal(v8, v8s)
+    assert torch.equal(sc, torch.cat([qs, ks, vs]))
+    x32 = [t.float().cpu().numpy() for t in xs]
+    kc, ksr = hadamard_quantize(x32[1])
+    qc, qsr = hadamard_quantize(x32[0], k_scale=ksr, softmax_scale=sm)
+    assert np.array_equal(k8.cpu().numpy(), kc) and np.array_equal(q8.cpu().numpy(), qc)
+    assert sc[0].item() == qsr and sc[1].item() == ksr
