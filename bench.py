@@ -13,6 +13,9 @@ Prints ONE JSON line. ``value`` is the algorithmic causal FLOP count
 B*Hq*S^2*(d_qk+d_v) divided by the measured time of a whole step, in TFLOP/s.
 The attention kernel alone is reported beside it and in ``roofline``, whose
 duration comes from HIP events recorded on the stream the kernel runs on.
+For FP8, the input step folds Q's scale so that the score factor is a power
+of two; ``attention_plain_q_scale`` times the same attention with Q under its
+plain per-tensor absmax scale (the kernel's fma form) beside it.
 ``cpu_baseline`` times the fp64 CPU oracle on the first four query heads of
 batch 0 of the same workload (all S query rows each), on this host's cores.
 
@@ -176,6 +179,60 @@ def sustained(seconds: float, attention, flops: float, stream, peak_tflops: floa
             # whole-socket energy (HBM and idle parts included) per unit of work
             rec["tflop_per_joule"] = round(rec["attention_tflops"] / float(np.median(pws)), 4)
     return rec
+
+
+def plain_q_scale_leg(steps: int, w, q32, codes, scales, o, flags: int, flops: float, peak: float, sm_scale: float,
+                      stream) -> dict:
+    """The FP8 attention again, with Q under its plain per-tensor absmax scale.
+
+    The input step folds Q's scale so that the score factor q_scale * k_scale
+    * softmax_scale * log2(e) is a power of two, which lets the kernel apply
+    it through the MFMA operand scales. With the plain scale the factor is
+    generally not a power of two and the kernel applies it with one fma per
+    score. Same K, V codes and scales; own Q codes, O and LSE buffers.
+    """
+    import numpy as np
+    import torch
+
+    from bf16_causal_prefill_fwd_amd import ops
+
+    print(f"# plain absmax Q scale: {steps} attention launches", file=sys.stderr, flush=True)
+    q_plain = torch.empty_like(codes[0])
+    scales_plain = torch.empty(3, dtype=torch.float32, device=q32.device)
+    ops.attn_quantize_fp8(q32, out=q_plain, scale=scales_plain[0:1], stream=stream)
+    scales_plain[1:].copy_(scales[1:])
+    o_plain = torch.empty_like(o)
+    lse_plain = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=q32.device)
+
+    def run():
+        ops.attn_prefill_fwd(q_plain, codes[1], codes[2], causal=w.causal, out=o_plain, lse=lse_plain,
+                             d_scales=scales_plain, stream=stream, flags=flags)
+
+    for _ in range(3):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    sc = scales_plain.cpu().tolist()
+    c = sc[0] * sc[1] * sm_scale * math.log2(math.e)
+    mant, _ = math.frexp(c)
+    avg = float(np.mean(ms))
+    tflops = flops / (avg * 1e-3) / 1e12
+    return {
+        "q_scale": sc[0],
+        "score_factor_power_of_two": bool(abs(mant - 0.5) < 2.0 ** -19),
+        "attention_ms": round(avg, 4),
+        "attention_ms_min": round(float(np.min(ms)), 4),
+        "attention_tflops": round(tflops, 2),
+        "attention_frac_of_peak": round(tflops / peak, 4),
+        "note": "Q quantized with its plain absmax/448 scale (attn_quantize_fp8); the headline uses the folded "
+                "query scale of attn_quantize_fp8_qkv",
+    }
 
 
 def cpu_baseline(w, q, k, v, n_heads: int = 4, hadamard: bool = False, o_gpu=None, lse_gpu=None) -> dict:
@@ -433,6 +490,10 @@ def main(argv=None) -> int:
         rec["sustained"] = sustained(args.sustain_s, attention, flops, stream, peak)
     else:
         rec["sustained"] = None
+    rec["attention_plain_q_scale"] = None
+    if w.dtype == "fp8" and not args.hadamard:
+        rec["attention_plain_q_scale"] = plain_q_scale_leg(args.steps, w, q32, codes, scales, o, flags, flops, peak,
+                                                           sm_scale, stream)
     if not args.no_cpu_baseline:
         print("# cpu baseline (fp64 oracle, four head slices)", file=sys.stderr, flush=True)
         nh = min(4, w.Hq)
