@@ -9,7 +9,9 @@
 //
 //  * One workgroup = 4 waves = 128 query rows of one (batch, head); each
 //    wave owns 32 rows and keeps its Q fragment in registers. Two workgroups
-//    share a CU, so each SIMD runs two independent waves.
+//    share a CU, so each SIMD runs two independent waves. (BF16 at d = 128:
+//    one workgroup of 8 waves = 256 rows per CU, which halves the staging
+//    traffic per FLOP; the two waves of a SIMD then share a barrier.)
 //  * Software pipeline inside each wave, one key tile of BN keys per step
 //    (64 for FP8, 32 for BF16): while the softmax of tile n runs on the vector ALU, the same wave
 //    issues the MFMAs of S^T = K.Q^T for tile n+1 and of O^T += V^T.P^T for
@@ -59,14 +61,17 @@ struct FwdParams {
   int xcd_remap;
 };
 
-template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_, bool STAGE_UNROLL_ = true, int LOOKAHEAD_ = 2>
+template <bool FP8_, int DQK_, int DV_, int BN_, int NSTAGE_, bool STAGE_UNROLL_ = true, int LOOKAHEAD_ = 2,
+          int NWAVES_ = 4>
 struct FwdCfg {
   static constexpr bool FP8 = FP8_;
   static constexpr int DQK = DQK_, DV = DV_, BN = BN_;
-  // 4-wave workgroups, two per CU (two waves per SIMD); each wave
-  // interleaves its MFMAs with its own softmax
-  static constexpr int NWAVES = 4;
-  static constexpr int WG_PER_CU = 2;
+  // two waves per SIMD: 4-wave workgroups two per CU, or 8-wave workgroups
+  // one per CU (twice the query rows per K/V tile staged, but the two waves
+  // of a SIMD meet at every barrier); each wave interleaves its MFMAs with
+  // its own softmax
+  static constexpr int NWAVES = NWAVES_;
+  static constexpr int WG_PER_CU = 8 / NWAVES;
   static constexpr int BM = 32 * NWAVES;             // query rows per workgroup
   static constexpr int NTHREADS = NWAVES * 64;
   static constexpr int EB = FP8 ? 1 : 2;             // bytes per element
@@ -104,6 +109,7 @@ struct FwdCfg {
   static_assert(KTILE % (16 * NTHREADS) == 0 && VTILE % (16 * NTHREADS) == 0, "staging split");
   static_assert(NSTAGE >= 2 && INFLIGHT < 64, "ring depth / vmcnt range");
   static_assert(!STAGE_UNROLL || NSTAGE % 2 == 0, "the stage index must carry the score parity");
+  static_assert(NWAVES == 4 || NWAVES == 8, "two waves per SIMD");
   static_assert(WG_PER_CU * LDS_BYTES <= 160 * 1024, "LDS of the workgroups of one CU");
 };
 
