@@ -324,6 +324,9 @@ def main(argv=None) -> int:
                     help="override the workload's input distribution (same shape), e.g. to compare the "
                          "clock and energy of Gaussian and heavy-tailed inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-plain-q-scale", action="store_true",
+                    help="skip the second FP8 attention timing with Q under its plain absmax scale (keeps a "
+                         "profiled run to the headline's launches)")
     ap.add_argument("--sustain-s", type=float, default=10.0,
                     help="seconds of back-to-back attention launches with SCLK sampling (0 = skip)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -491,7 +494,7 @@ def main(argv=None) -> int:
     else:
         rec["sustained"] = None
     rec["attention_plain_q_scale"] = None
-    if w.dtype == "fp8" and not args.hadamard:
+    if w.dtype == "fp8" and not args.hadamard and not args.no_plain_q_scale:
         rec["attention_plain_q_scale"] = plain_q_scale_leg(args.steps, w, q32, codes, scales, o, flags, flops, peak,
                                                            sm_scale, stream)
     if not args.no_cpu_baseline:

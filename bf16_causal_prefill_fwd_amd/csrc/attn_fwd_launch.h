@@ -11,9 +11,15 @@ using CfgF8D128 = FwdCfg<true, 128, 128, 64, 4>;
 // registers of two waves per SIMD only with one MFMA job's operand reads in
 // flight instead of two)
 using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4, true, 1>;
-// (BF16 d_qk = 128: 8-wave workgroups, one per CU; measured 1.5-1.7% faster
-// than two 4-wave ones on the 16K GQA layer, where FP8 is 0.2-1.8% slower)
-using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4, true, 2, 8>;
+using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4>;
+// BF16 d_qk = 128 in 8-wave workgroups (256 query rows, one per CU): half
+// the K/V staging per FLOP. Measured 1.5-1.9% faster than two 4-wave ones on
+// the 16K GQA layer and about 4% faster from 8K to 64K tokens (FP8: 0.2-1.8%
+// slower), but slower on small grids (+9% at 4K, +39% at 1K tokens with 32
+// heads), so it runs when its grid has at least 4 workgroups per CU of the
+// 256 (8K tokens and 32 heads make 1,024).
+using CfgBFD128W8 = FwdCfg<false, 128, 128, 32, 4, true, 2, 8>;
+constexpr int64_t kWave8MinWorkgroups = 1024;
 using CfgBFD192 = FwdCfg<false, 192, 128, 32, 4>;
 
 enum LaunchStatus { kLaunched = 0, kTooManyWorkgroups = 1, kLaunchFailed = 2 };
@@ -41,7 +47,10 @@ inline LaunchStatus launch_attn_fwd(FwdParams prm, bool fp8, int d_qk, int pmode
     return d_qk == 128 ? launch_fwd<CfgF8D128, kPLean>(prm, stream) : launch_fwd<CfgF8D192, kPLean>(prm, stream);
   if (fp8)
     return d_qk == 128 ? launch_fwd<CfgF8D128, kPExact>(prm, stream) : launch_fwd<CfgF8D192, kPExact>(prm, stream);
-  return d_qk == 128 ? launch_fwd<CfgBFD128, kPExact>(prm, stream) : launch_fwd<CfgBFD192, kPExact>(prm, stream);
+  if (d_qk == 192) return launch_fwd<CfgBFD192, kPExact>(prm, stream);
+  const int64_t wg8 = (int64_t)prm.B * prm.Hq * ((prm.S + CfgBFD128W8::BM - 1) / CfgBFD128W8::BM);
+  return wg8 >= kWave8MinWorkgroups ? launch_fwd<CfgBFD128W8, kPExact>(prm, stream)
+                                    : launch_fwd<CfgBFD128, kPExact>(prm, stream);
 }
 
 }  // namespace attn

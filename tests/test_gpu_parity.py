@@ -112,6 +112,9 @@ ZERO_Q = [
     (1, 300, 2, 2, 128),
     (2, 1087, 16, 4, 128),
     (2, 1087, 16, 4, 192),
+    # a grid large enough for BF16's 8-wave workgroups (33 x 32 >= 1,024 of
+    # them), ragged: the last 256-row tile holds 77 rows
+    (1, 8269, 32, 8, 128),
 ]
 
 
@@ -190,6 +193,35 @@ def sample_rows(w: Workload, rng: np.random.Generator, n_heads: int = 6):
         for i in sorted(set([p for p in pos if 0 <= p < w.S] + list(extra))):
             rows.append((int(rng.integers(0, w.B)), int(h), int(i)))
     return rows
+
+
+# BF16 d = 128 runs 8-wave workgroups (256 query rows) once that grid has at
+# least 1,024 of them, 4-wave ones below: these lengths with 32 query heads are
+# past the switch (33 to 34 tiles of 256 rows per head) and put every ragged
+# tail of a 256-row tile and of a 32-key step through the 8-wave kernel
+EIGHT_WAVE_S = [8193, 8223, 8225, 8447, 8640]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_bf16_eight_wave_workgroups_sampled_rows(causal):
+    worst = (0.0, 0.0)
+    for S in EIGHT_WAVE_S if causal else EIGHT_WAVE_S[-1:]:
+        w = Workload(f"bf16_w8_{S}", 1, S, 32, 8, 128, 128, "bf16", "gauss", causal=causal)
+        assert w.B * w.Hq * -(-S // 256) >= 1024
+        q, k, v, o, lse, ex = run_case(w, seed=S)
+        rows = sample_rows(w, np.random.default_rng(S), n_heads=4)
+        ref = prefill_reference(q, k, v, "bf16", causal=causal, rows=rows)
+        bi = torch.tensor([r[0] for r in rows]); hi = torch.tensor([r[1] for r in rows])
+        ii = torch.tensor([r[2] for r in rows])
+        og = o[bi, ii, hi].float().cpu().numpy().astype(np.float64)
+        lg = lse[bi, hi, ii].cpu().numpy().astype(np.float64)
+        err, _ = check_o(og, ref["o_rows"], "bf16", f"S={S} {len(rows)} rows: ")
+        lerr = float(np.max(np.abs(lg - ref["lse_rows"])))
+        assert lerr <= LSE_TOL, (S, lerr)
+        worst = (max(worst[0], err), max(worst[1], lerr))
+        o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], causal=causal)
+        assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(l2, lse)
+    print(f"  worst: O rel-L2 {worst[0]:.3e}  LSE max-abs {worst[1]:.3e}", flush=True)
 
 
 # every workload with the pipeline's folded query scale; the FP8 layers also
