@@ -56,7 +56,8 @@ SMALL = [
     Workload("batch4_xcd_order_bf16", 4, 100, 4, 2, 128, 128, "bf16", "gauss"),
     Workload("single_row_fp8", 1, 1, 2, 2, 128, 128, "fp8", "gauss"),
     Workload("ragged_mla_fp8", 1, 333, 4, 4, 192, 128, "fp8", "mla"),
-    # long enough for the MLA kernel's unchecked loop part (two-step loop)
+    # long enough for the FP8 MLA kernel's unchecked loop part (9 or more full
+    # 64-key tiles; loop unrolled by the ring depth, one MFMA job of look-ahead)
     Workload("mla_fp8_unchecked_loop", 1, 700, 2, 2, 192, 128, "fp8", "mla"),
     Workload("ragged_gqa_bf16", 1, 333, 8, 2, 128, 128, "bf16", "gauss"),
     Workload("batch2_bf16", 2, 129, 2, 2, 128, 128, "bf16", "gauss"),
