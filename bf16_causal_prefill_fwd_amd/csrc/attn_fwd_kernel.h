@@ -95,6 +95,8 @@ struct FwdCfg {
   // folded score form available (the scaled MFMA exists for FP8 only)
   static constexpr bool FOLDABLE = FP8;
   static constexpr int LDS_BYTES = NSTAGE * (KTILE + VTILE);
+  // the V ring (after the K ring) ends past the 16-bit ds_read offset
+  static constexpr bool V_ABS = LDS_BYTES > 65536;
   static constexpr int NST = BN / 32;                // 32-key score tiles
   static constexpr int NOT = DV / 32;                // 32-wide output tiles
   static constexpr int QK_STEPS = FP8 ? DQK / 64 : DQK / 16;
@@ -447,6 +449,9 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       const int dv0 = 32 * tv + 16 * (hh & 1);
       const int ch = C::FP8 ? dv0 / 16 : dv0 / 8 + ((kk & 3) >> 1);
       v_off[tv] = krow_lane * C::VROW + 16 * v_swz<C::VCH>(ch, krow_lane) + 8 * (kk & 1);
+      // V ring ending past 64 KiB: the lane's base holds the ring's address,
+      // so each read's immediate carries only the stage and key offsets
+      if constexpr (C::V_ABS) v_off[tv] = pin((int)v_lds_addr + v_off[tv]);
     }
   }
 
@@ -519,15 +524,21 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int key0 = 64 * u + 32 * (rr >> 1) + 16 * (rr & 1);
-          i32x2 x = lds_read_tr8(vl + key0 * C::VROW + v_off[tv]);
+          i32x2 x = C::V_ABS ? lds_read_tr8(lds_at((uint32_t)(v_off[tv] + (int)(vl - v_lds) + key0 * C::VROW)))
+                             : lds_read_tr8(vl + key0 * C::VROW + v_off[tv]);
           a[2 * rr] = x[0];
           a[2 * rr + 1] = x[1];
         }
       } else {
         // two transposed reads of 4 elements each, concatenated (element e
         // of the operand is 16-bit lane e of the pair)
-        const i32x2 x0 = __builtin_bit_cast(i32x2, lds_read_tr16(vl + (16 * u) * C::VROW + v_off[tv]));
-        const i32x2 x1 = __builtin_bit_cast(i32x2, lds_read_tr16(vl + (16 * u + 8) * C::VROW + v_off[tv]));
+        const int so = (int)(vl - v_lds);
+        const i32x2 x0 = __builtin_bit_cast(
+            i32x2, C::V_ABS ? lds_read_tr16(lds_at((uint32_t)(v_off[tv] + so + (16 * u) * C::VROW)))
+                            : lds_read_tr16(vl + (16 * u) * C::VROW + v_off[tv]));
+        const i32x2 x1 = __builtin_bit_cast(
+            i32x2, C::V_ABS ? lds_read_tr16(lds_at((uint32_t)(v_off[tv] + so + (16 * u + 8) * C::VROW)))
+                            : lds_read_tr16(vl + (16 * u + 8) * C::VROW + v_off[tv]));
         a = i32x4{x0[0], x0[1], x1[0], x1[1]};
       }
     } else {

@@ -100,6 +100,9 @@ __device__ __forceinline__ float pow2i(int e) { return __int_as_float((e + 127) 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS pointer from a byte address.
+__device__ __forceinline__ const ATTN_LDS char* lds_at(uint32_t a) { return (const ATTN_LDS char*)(uintptr_t)a; }
+
 // Byte address of an LDS object (what M0 and ds_* address operands hold).
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return (uint32_t)(uintptr_t)(const ATTN_LDS void*)p;

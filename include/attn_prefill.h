@@ -31,8 +31,10 @@
  *    checks run on the host before anything is enqueued; a failed check
  *    enqueues nothing. ATTN_ERR_HIP reports a launch failure
  *    (hipGetLastError after the launch).
- *  - Runs are deterministic: no atomics touch values, each output element
- *    has one fixed reduction order, so repeated launches are bit-identical.
+ *  - Runs are deterministic: each output element has one fixed reduction
+ *    order, and the only atomics are the quantizers' integer maxima of
+ *    absmax bits, whose result does not depend on their order, so repeated
+ *    launches are bit-identical.
  */
 #ifndef ATTN_PREFILL_H
 #define ATTN_PREFILL_H
