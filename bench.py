@@ -317,6 +317,9 @@ def main(argv=None) -> int:
                     help="FP8: rotate Q and K by Hadamard blocks in the input step (attn_quantize_fp8_qkv_hadamard)")
     ap.add_argument("--p-block-scale", action="store_true",
                     help="FP8: per (row, 64-key block) power-of-two scaling of P (ATTN_FLAG_P_BLOCK_SCALE)")
+    ap.add_argument("--p-rounded-sum", action="store_true",
+                    help="FP8, with --p-block-scale: O divided by the row sum of the rounded P from one more "
+                         "MFMA per step (ATTN_FLAG_P_ROUNDED_SUM)")
     ap.add_argument("--seq-len", type=int, default=None, help="override the workload's sequence length")
     ap.add_argument("--heads", type=int, default=None,
                     help="override the head count: Hq = Hkv = HEADS (multi-head attention)")
@@ -383,10 +386,14 @@ def main(argv=None) -> int:
 
     sm_scale = 1.0 / math.sqrt(w.d_qk)
 
-    if (args.hadamard or args.p_block_scale) and w.dtype != "fp8":
-        print("--hadamard and --p-block-scale apply to FP8 workloads only", file=sys.stderr)
+    if args.p_rounded_sum and not args.p_block_scale:
+        print("--p-rounded-sum needs --p-block-scale", file=sys.stderr)
         return 2
-    flags = ops.ATTN_FLAG_P_BLOCK_SCALE if args.p_block_scale else 0
+    if (args.hadamard or args.p_block_scale or args.p_rounded_sum) and w.dtype != "fp8":
+        print("--hadamard, --p-block-scale and --p-rounded-sum apply to FP8 workloads only", file=sys.stderr)
+        return 2
+    flags = (ops.ATTN_FLAG_P_BLOCK_SCALE if args.p_block_scale else 0) | \
+        (ops.ATTN_FLAG_P_ROUNDED_SUM if args.p_rounded_sum else 0)
 
     def input_step():
         if w.dtype == "fp8":
@@ -465,6 +472,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "B": w.B, "S": w.S, "Hq": w.Hq, "Hkv": w.Hkv, "d_qk": w.d_qk,
                    "d_v": w.d_v, "causal": w.causal, "dist": w.dist, "seed": args.seed,
                    "hadamard": bool(args.hadamard), "p_block_scale": bool(args.p_block_scale),
+                   "p_rounded_sum": bool(args.p_rounded_sum),
                    "step": "input step (quantize/cast Q,K,V) + attention"},
         "attention_ms": round(attn_avg, 4),
         "attention_ms_min": round(float(np.min(attn_ms)), 4),

@@ -258,7 +258,7 @@ enum ScoreForm { kScaleFma = 0, kScaleFolded = 1 };
 //    back by the P operand's E8M0 scale, that keeps every block's largest
 //    code in (96, 104]; O is divided by the sum of the same rounded
 //    probabilities, taken by one more MFMA (P times a block of ones).
-enum PMode { kPExact = 0, kPBlockScaled = 1, kPLean = 2 };
+enum PMode { kPExact = 0, kPBlockScaled = 1, kPLean = 2, kPBlockScaledRoundedSum = 3 };
 
 // Lean P: a block's largest code is re-aimed into (kLeanTarget - 8,
 // kLeanTarget] when it leaves [kLeanLow, kLeanHigh] (code 127 is a NaN, 128
@@ -280,12 +280,16 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   const uint32_t v_lds_addr = lds_address(v_ring);
   constexpr bool FOLD = FORM == kScaleFolded;
   static_assert(!FOLD || C::FP8, "scale folding needs the scaled FP8 MFMA");
-  constexpr bool PS = PM == kPBlockScaled;
+  constexpr bool PS = PM == kPBlockScaled || PM == kPBlockScaledRoundedSum;
   constexpr bool LEAN = PM == kPLean;
+  // O divided by the sum of the rounded probabilities the P.V MFMAs take
+  // (one more MFMA per step: P times a ones operand); Lean P always
+  constexpr bool RSUM = LEAN || PM == kPBlockScaledRoundedSum;
   static_assert(!(LEAN && FOLD), "Lean P forms its codes with one fma per score: the fma form");
-  static_assert(!(PS || LEAN) || C::FP8, "block-scaled and Lean P need the scaled FP8 MFMA");
-  // scaled MFMAs are not matched by scheduling groups: fences order the jobs
-  constexpr bool FENCED = FOLD || PS || LEAN;
+  static_assert(!(PS || RSUM) || C::FP8, "block-scaled P, Lean P and the rounded row sum need the FP8 MFMA");
+  // scaled MFMAs (and the extra row-sum MFMA) are not matched by scheduling
+  // groups: fences order the jobs
+  constexpr bool FENCED = FOLD || PS || RSUM;
 
   constexpr int BN = C::BN, DV = C::DV, NS = C::NSTAGE;
   const int tid = threadIdx.x;
@@ -481,10 +485,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // largest shift, where its zeros stay zeros.
   float kb_div = 1.f;
   int e8[2] = {127, 127};
-  // Lean P: the shift kb of the tile being converted, the code bias of the
-  // scores (56 + 8 (kb - m_ref), m_ref the integer reference of O, so the
-  // code of a score s is 8 c s + bias), and the row sum of the rounded
-  // probabilities (every register of lacc holds it).
+  // Lean P: the shift kb of the tile being converted and the code bias of
+  // the scores (56 + 8 (kb - m_ref), m_ref the integer reference of O, so
+  // the code of a score s is 8 c s + bias). Lean P and the rounded-sum
+  // modes: the row sum of the rounded probabilities (every register of lacc
+  // holds it).
   int kb = 0;
   float cbias = 0.f;
   f32x16 lacc = f32x16{};
@@ -565,7 +570,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       if constexpr (C::FP8) {
         i32x8 pop = {pv[0][0], pv[0][1], pv[0][2], pv[0][3], pv[1][0], pv[1][1], pv[1][2], pv[1][3]};
         oacc[tv] = (PS || LEAN) ? mfma_f8_scaled(a, pop, oacc[tv], 127, e8[PP]) : mfma_f8(a, pop, oacc[tv]);
-        if constexpr (LEAN) {
+        if constexpr (RSUM) {
           if (j == 0) lacc = mfma_f8_scaled(ones8, pop, lacc, 127, e8[PP]);
         }
       } else {
@@ -682,6 +687,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
+      if constexpr (RSUM) lacc *= alpha;
 #pragma unroll
       for (int c = 0; c < NCHUNK; ++c) probs_chunk(c, Pc, m_run, lsum, False_{});
     } else {
@@ -695,6 +701,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
       l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < C::NOT; ++t) oacc[t] *= alpha;
+      if constexpr (RSUM) lacc *= alpha;
 #pragma unroll
       for (int i = 0; i < 16; ++i) cblk[i] = -m_run;
 #pragma unroll
@@ -919,10 +926,12 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   }
   wait_vmcnt<0>();  // drain the loads of the last steps before the workgroup ends
 
-  // ---- epilogue: O = O_acc * v_scale / l, LSE = ln2 * (m + log2 l)
-  // (Lean P: the rounded probabilities' row sum, over both key halves)
+  // ---- epilogue: O = O_acc * v_scale / l, LSE = ln2 * (m + log2 l), with
+  // l the fp32 sum of the exact exponentials over both key halves; O is
+  // divided instead by the rounded probabilities' row sum where that is kept
+  // (Lean P has no other)
   const float l_tot = LEAN ? lacc[0] : l_run + swap_halves(l_run);
-  const float inv = vs / l_tot;
+  const float inv = vs / (RSUM ? lacc[0] : l_tot);
   if (qrow < S) {
     uint16_t* op = p.o + (((int64_t)b * S + qrow) * p.Hq + h) * DV;
 #pragma unroll
@@ -958,7 +967,9 @@ __global__ __launch_bounds__(C::NTHREADS, C::WG_PER_CU) void attn_fwd_kernel(Fwd
   }
   // scores in log2 units: t = c * (q . k)
   const float c_log2 = qs * ks * p.sm_scale * 1.4426950408889634f;
-  if constexpr (C::FOLDABLE && PM != kPLean) {
+  // (Lean P and the rounded-sum modes take the fma form only: with the
+  // folded form's -m block their extra registers do not fit)
+  if constexpr (C::FOLDABLE && PM != kPLean && PM != kPBlockScaledRoundedSum) {
     // c = f * 2^e, f in [0.5, 1): a power of two up to fp32 rounding of the
     // scale product (a relative 2^-18 covers it many times over)
     int e;

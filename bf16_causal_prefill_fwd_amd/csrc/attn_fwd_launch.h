@@ -43,6 +43,9 @@ inline LaunchStatus launch_attn_fwd(FwdParams prm, bool fp8, int d_qk, int pmode
   if (fp8 && pmode == kPBlockScaled)
     return d_qk == 128 ? launch_fwd<CfgF8D128, kPBlockScaled>(prm, stream)
                        : launch_fwd<CfgF8D192, kPBlockScaled>(prm, stream);
+  if (fp8 && pmode == kPBlockScaledRoundedSum)
+    return d_qk == 128 ? launch_fwd<CfgF8D128, kPBlockScaledRoundedSum>(prm, stream)
+                       : launch_fwd<CfgF8D192, kPBlockScaledRoundedSum>(prm, stream);
   if (fp8 && pmode == kPLean)
     return d_qk == 128 ? launch_fwd<CfgF8D128, kPLean>(prm, stream) : launch_fwd<CfgF8D192, kPLean>(prm, stream);
   if (fp8)

@@ -22,6 +22,7 @@ ATTN_DTYPE_FP8_E4M3 = 0
 ATTN_DTYPE_BF16 = 1
 ATTN_FLAG_P_BLOCK_SCALE = 1
 ATTN_FLAG_LEAN_P = 2
+ATTN_FLAG_P_ROUNDED_SUM = 4
 
 _lib = None
 

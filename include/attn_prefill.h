@@ -108,6 +108,22 @@ enum {
    * ATTN_ERR_UNSUPPORTED.
    */
   ATTN_FLAG_LEAN_P = 2,
+  /*
+   * FP8 only, together with ATTN_FLAG_P_BLOCK_SCALE (alone, or with
+   * ATTN_FLAG_LEAN_P: ATTN_ERR_INVALID): O is divided by the row sum of the
+   * rounded, block-scaled probabilities that the P.V products take,
+   * accumulated by one more MFMA per 64-key step (P times an operand of
+   * e4m3 ones, under P's power-of-two scale), instead of by the fp32 sum of
+   * the exact exponentials (aicronaca.it, "Perché l'FP8 non basta da solo";
+   * ai4bro.com, "How does ZYFA work?": the row sum from one extra MFMA). The
+   * rounding of each row's largest probabilities then cancels between O and
+   * its normalizer, which lowers the O error on heavy-tailed inputs. The
+   * block scaling is required: without it, probabilities far below a row's
+   * running maximum underflow in e4m3 and drop out of the rounded sum. LSE
+   * still comes from the fp32 exact sum. This mode applies the score factor
+   * with one fma per score whatever the query scale.
+   */
+  ATTN_FLAG_P_ROUNDED_SUM = 4,
 };
 
 /*

@@ -145,9 +145,10 @@ int main() {
   }
   std::vector<uint8_t> hv8(nkv);
   float hs[3];
-  // exact probabilities, then the block-scaled form (for Q = 0 every p is 1,
-  // exact under any power-of-two scaling)
-  for (int flags : {0, (int)ATTN_FLAG_P_BLOCK_SCALE}) {
+  // exact probabilities, the block-scaled form, and that with the rounded-sum
+  // normalizer (for Q = 0 every p is 1, exact under any power-of-two
+  // scaling, and the rounded row sum is exact)
+  for (int flags : {0, (int)ATTN_FLAG_P_BLOCK_SCALE, (int)(ATTN_FLAG_P_ROUNDED_SUM | ATTN_FLAG_P_BLOCK_SCALE)}) {
     ATTN_OK_(attn_prefill_fwd_ex(q8, k8, v8, dout, dlse, 1.f, 1.f, 1.f, dscales, sm, B, S, HQ, HKV, D, D, 1,
                                  ATTN_DTYPE_FP8_E4M3, flags, st));
     HIP_OK(hipMemcpyAsync(hv8.data(), v8, nkv, hipMemcpyDeviceToHost, st));
@@ -156,7 +157,10 @@ int main() {
     HIP_OK(hipMemcpyAsync(lse.data(), dlse, lse.size() * 4, hipMemcpyDeviceToHost, st));
     HIP_OK(hipStreamSynchronize(st));
     for (size_t i = 0; i < nkv; ++i) vdeq[i] = e4m3fn_value(hv8[i]) * hs[2];
-    if (check(flags ? "fp8 block-scaled P" : "fp8", o, lse, vdeq)) return 1;
+    const char* what = flags == 0                              ? "fp8"
+                       : flags == (int)ATTN_FLAG_P_BLOCK_SCALE ? "fp8 block-scaled P"
+                                                               : "fp8 block-scaled P, rounded-sum normalizer";
+    if (check(what, o, lse, vdeq)) return 1;
   }
 
   // ---- BF16: RNE casts, then the same closed form

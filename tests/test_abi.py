@@ -86,6 +86,13 @@ def test_fwd_ex_flags():
     assert f(*args[:4], FAKE, *args[5:], 0, ops.ATTN_FLAG_LEAN_P, None) == INVALID
     assert f(*args, 0, ops.ATTN_FLAG_LEAN_P | ops.ATTN_FLAG_P_BLOCK_SCALE, None) == INVALID
     assert f(*args, 0, ops.ATTN_FLAG_LEAN_P, None) == UNSUPPORTED
+    # the rounded-sum normalizer: FP8 only, only with block-scaled P, not with
+    # Lean P (which has it built in)
+    RSPS = ops.ATTN_FLAG_P_ROUNDED_SUM | ops.ATTN_FLAG_P_BLOCK_SCALE
+    assert f(*args, 1, RSPS, None) == UNSUPPORTED
+    assert f(*args, 0, ops.ATTN_FLAG_P_ROUNDED_SUM, None) == INVALID
+    assert f(*args, 0, ops.ATTN_FLAG_LEAN_P | ops.ATTN_FLAG_P_ROUNDED_SUM, None) == INVALID
+    assert f(*args[:4], FAKE + 2, *args[5:], 0, RSPS, None) == INVALID  # misaligned lse
 
 
 def test_quantize_q_rejects_bad_arguments():
