@@ -10,7 +10,7 @@
 //  * One workgroup = 4 waves = 128 query rows of one (batch, head); each
 //    wave owns 32 rows and keeps its Q fragment in registers. Two workgroups
 //    share a CU, so each SIMD runs two independent waves. (BF16 at d = 128
-//    on large grids: one workgroup of 8 waves = 256 rows per CU, which
+//    on long sequences: one workgroup of 8 waves = 256 rows per CU, which
 //    halves the staging traffic per FLOP; the two waves of a SIMD then share
 //    a barrier.)
 //  * Software pipeline inside each wave, one key tile of BN keys per step

@@ -14,11 +14,14 @@ using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4, true, 1>;
 using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4>;
 // BF16 d_qk = 128 in 8-wave workgroups (256 query rows, one per CU): half
 // the K/V staging per FLOP. Measured 1.5-1.9% faster than two 4-wave ones on
-// the 16K GQA layer and about 4% faster from 8K to 64K tokens (FP8: 0.2-1.8%
-// slower), but slower on small grids (+9% at 4K, +39% at 1K tokens with 32
-// heads), so it runs when its grid has at least 4 workgroups per CU of the
-// 256 (8K tokens and 32 heads make 1,024).
+// the 16K GQA layer and up to 4% from 16K to 64K tokens (FP8: 0.2-1.8%
+// slower). It loses on short rows, where the taller tile's causal diagonal
+// (every wave runs every step of its workgroup) outweighs the staging (+4%
+// at 4K, +18% at 1K and 512 tokens, however many sequences), and on small
+// grids (+39% at 1K tokens and 32 heads, B = 1). So it runs from 8K tokens,
+// when its grid has at least 4 workgroups per CU of the 256.
 using CfgBFD128W8 = FwdCfg<false, 128, 128, 32, 4, true, 2, 8>;
+constexpr int kWave8MinSeq = 8192;
 constexpr int64_t kWave8MinWorkgroups = 1024;
 using CfgBFD192 = FwdCfg<false, 192, 128, 32, 4>;
 
@@ -52,8 +55,8 @@ inline LaunchStatus launch_attn_fwd(FwdParams prm, bool fp8, int d_qk, int pmode
     return d_qk == 128 ? launch_fwd<CfgF8D128, kPExact>(prm, stream) : launch_fwd<CfgF8D192, kPExact>(prm, stream);
   if (d_qk == 192) return launch_fwd<CfgBFD192, kPExact>(prm, stream);
   const int64_t wg8 = (int64_t)prm.B * prm.Hq * ((prm.S + CfgBFD128W8::BM - 1) / CfgBFD128W8::BM);
-  return wg8 >= kWave8MinWorkgroups ? launch_fwd<CfgBFD128W8, kPExact>(prm, stream)
-                                    : launch_fwd<CfgBFD128, kPExact>(prm, stream);
+  return prm.S >= kWave8MinSeq && wg8 >= kWave8MinWorkgroups ? launch_fwd<CfgBFD128W8, kPExact>(prm, stream)
+                                                            : launch_fwd<CfgBFD128, kPExact>(prm, stream);
 }
 
 }  // namespace attn

@@ -196,10 +196,11 @@ def sample_rows(w: Workload, rng: np.random.Generator, n_heads: int = 6):
     return rows
 
 
-# BF16 d = 128 runs 8-wave workgroups (256 query rows) once that grid has at
-# least 1,024 of them, 4-wave ones below: these lengths with 32 query heads are
-# past the switch (33 to 34 tiles of 256 rows per head) and put every ragged
-# tail of a 256-row tile and of a 32-key step through the 8-wave kernel
+# BF16 d = 128 runs 8-wave workgroups (256 query rows) from 8,192 tokens when
+# that grid has at least 1,024 of them, 4-wave ones otherwise: these lengths
+# with 32 query heads are past the switch (33 to 34 tiles of 256 rows per head)
+# and put every ragged tail of a 256-row tile and of a 32-key step through the
+# 8-wave kernel
 EIGHT_WAVE_S = [8193, 8223, 8225, 8447, 8640]
 
 
@@ -208,7 +209,7 @@ def test_bf16_eight_wave_workgroups_sampled_rows(causal):
     worst = (0.0, 0.0)
     for S in EIGHT_WAVE_S if causal else EIGHT_WAVE_S[-1:]:
         w = Workload(f"bf16_w8_{S}", 1, S, 32, 8, 128, 128, "bf16", "gauss", causal=causal)
-        assert w.B * w.Hq * -(-S // 256) >= 1024
+        assert S >= 8192 and w.B * w.Hq * -(-S // 256) >= 1024
         q, k, v, o, lse, ex = run_case(w, seed=S)
         rows = sample_rows(w, np.random.default_rng(S), n_heads=4)
         ref = prefill_reference(q, k, v, "bf16", causal=causal, rows=rows)
