@@ -75,6 +75,12 @@ SMALL = [
     # 16 query heads per kv head: one XCD unit spans 16 query heads
     Workload("gqa_group16_fp8", 1, 300, 16, 1, 128, 128, "fp8", "outlier"),
     Workload("gqa_group8_bf16", 2, 150, 16, 2, 128, 128, "bf16", "gauss"),
+    # group sizes that are not powers of two, under the plain tile-major order
+    # (B * Hkv = 2) and the XCD order (B * Hkv = 8)
+    Workload("gqa_group6_fp8", 1, 1000, 12, 2, 128, 128, "fp8", "outlier"),
+    Workload("mla_group3_fp8", 1, 600, 6, 2, 192, 128, "fp8", "mla"),
+    Workload("xcd_order_group3_fp8", 1, 300, 24, 8, 128, 128, "fp8", "gauss"),
+    Workload("xcd_order_group3_bf16", 1, 300, 24, 8, 128, 128, "bf16", "outlier"),
 ]
 
 
@@ -224,6 +230,30 @@ def test_bf16_eight_wave_workgroups_sampled_rows(causal):
         o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], causal=causal)
         assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(l2, lse)
     print(f"  worst: O rel-L2 {worst[0]:.3e}  LSE max-abs {worst[1]:.3e}", flush=True)
+
+
+# the 8-wave BF16 kernel under both work orders: two sequences with B * Hkv = 8
+# (whole kv units per XCD) and G = 6 query heads per kv head with B * Hkv = 6
+# (plain tile-major order)
+EIGHT_WAVE_ORDERS = [Workload("bf16_w8_batch2_xcd_order", 2, 8200, 16, 4, 128, 128, "bf16", "gauss"),
+                     Workload("bf16_w8_group6_plain_order", 1, 8300, 36, 6, 128, 128, "bf16", "outlier")]
+
+
+@pytest.mark.parametrize("w", EIGHT_WAVE_ORDERS, ids=[w.name for w in EIGHT_WAVE_ORDERS])
+def test_bf16_eight_wave_work_orders_sampled_rows(w):
+    assert w.S >= 8192 and w.B * w.Hq * -(-w.S // 256) >= 1024
+    q, k, v, o, lse, ex = run_case(w, seed=w.S)
+    rows = sample_rows(w, np.random.default_rng(w.S), n_heads=4)
+    assert len({r[0] for r in rows}) == w.B
+    ref = prefill_reference(q, k, v, "bf16", rows=rows)
+    bi = torch.tensor([r[0] for r in rows]); hi = torch.tensor([r[1] for r in rows])
+    ii = torch.tensor([r[2] for r in rows])
+    og = o[bi, ii, hi].float().cpu().numpy().astype(np.float64)
+    lg = lse[bi, hi, ii].cpu().numpy().astype(np.float64)
+    check_o(og, ref["o_rows"], "bf16", f"{len(rows)} rows: ")
+    lerr = float(np.max(np.abs(lg - ref["lse_rows"])))
+    print(f"  LSE max-abs {lerr:.3e}", flush=True)
+    assert lerr <= LSE_TOL
 
 
 # every workload with the pipeline's folded query scale; the FP8 layers also
