@@ -72,6 +72,8 @@ SMALL = [
     Workload("noncausal_fp8", 1, 300, 4, 2, 128, 128, "fp8", "gauss", causal=False),
     Workload("noncausal_bf16", 1, 200, 2, 1, 128, 128, "bf16", "gauss", causal=False),
     Workload("noncausal_mla_fp8", 1, 150, 2, 2, 192, 128, "fp8", "mla", causal=False),
+    # the FP8 MLA kernel's unchecked loop part without the causal mask
+    Workload("noncausal_mla_fp8_700", 1, 700, 2, 2, 192, 128, "fp8", "mla", causal=False),
     # 16 query heads per kv head: one XCD unit spans 16 query heads
     Workload("gqa_group16_fp8", 1, 300, 16, 1, 128, 128, "fp8", "outlier"),
     Workload("gqa_group8_bf16", 2, 150, 16, 2, 128, 128, "bf16", "gauss"),
@@ -340,25 +342,30 @@ def test_noncausal_through_the_unchecked_loop(dtype):
         assert lerr <= LSE_TOL, (S, lerr)
 
 
-@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
-def test_running_max_grows_every_tile(dtype):
+RISING = [("fp8", 128, True), ("fp8", 128, False), ("bf16", 128, True),
+          ("fp8", 192, True), ("fp8", 192, False), ("bf16", 192, True)]
+
+
+@pytest.mark.parametrize("dtype,dqk,fold_q", RISING,
+                         ids=[f"{t}_d{d}" + ("" if f else "_plain_q") for t, d, f in RISING])
+def test_running_max_grows_every_tile(dtype, dqk, fold_q):
     # scores rise with the key index (k_j = (0.5 + 2j/S) * u, q_i = 4 u for a
     # random unit-scale u), so each new tile holds the row's largest score
     # and the exact-maximum path (running-max update, O and l rescale) runs
     # on nearly every step
     S, H = 700, 2
     rng = np.random.default_rng(21)
-    u = rng.standard_normal(128).astype(np.float32)
+    u = rng.standard_normal(dqk).astype(np.float32)
     u /= np.float32(np.linalg.norm(u) / np.sqrt(128))
     ramp = (0.5 + 2.0 * np.arange(S, dtype=np.float32) / S)[None, :, None, None]
-    k = np.ascontiguousarray(np.broadcast_to(ramp * u, (1, S, H, 128))).astype(np.float32)
+    k = np.ascontiguousarray(np.broadcast_to(ramp * u, (1, S, H, dqk))).astype(np.float32)
     k += 0.05 * rng.standard_normal(k.shape).astype(np.float32)
-    q = np.ascontiguousarray(np.broadcast_to(4.0 * u, (1, S, H, 128))).astype(np.float32)
+    q = np.ascontiguousarray(np.broadcast_to(4.0 * u, (1, S, H, dqk))).astype(np.float32)
     v = rng.standard_normal((1, S, H, 128)).astype(np.float32)
-    print(f"case rising scores {dtype} S={S}", flush=True)
-    o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), dtype)
+    print(f"case rising scores {dtype} S={S} d_qk={dqk} fold_q={fold_q}", flush=True)
+    o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), dtype, fold_q=fold_q)
     torch.cuda.synchronize()
-    ref = prefill_reference(q, k, v, dtype, fold_q=True)
+    ref = prefill_reference(q, k, v, dtype, fold_q=fold_q)
     check_o(o.float().cpu().numpy().astype(np.float64), ref["o"], dtype)
     lerr = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref["lse"])))
     print(f"  LSE max-abs {lerr:.3e}", flush=True)
