@@ -152,6 +152,25 @@ def test_zero_query_gives_running_mean(dtype, shape):
     assert np.allclose(og[:, 0], np.repeat(vd[:, 0], G, axis=1), rtol=2 ** -8, atol=0)
 
 
+# lse = NULL skips the LSE output only: O keeps every bit, in every kernel and
+# P mode that takes an LSE
+O_ONLY = [("fp8", 128, 0), ("fp8", 192, 0), ("bf16", 128, 0), ("bf16", 192, 0),
+          ("fp8", 128, ops.ATTN_FLAG_P_BLOCK_SCALE),
+          ("fp8", 192, ops.ATTN_FLAG_P_BLOCK_SCALE | ops.ATTN_FLAG_P_ROUNDED_SUM)]
+
+
+@pytest.mark.parametrize("dtype,dqk,flags", O_ONLY, ids=[f"{t}_d{d}_flags{f}" for t, d, f in O_ONLY])
+def test_output_without_lse_is_unchanged(dtype, dqk, flags):
+    w = Workload("o_only", 1, 777, 4, 2, dqk, 128, dtype, "gauss")
+    q, k, v = make_inputs(w, seed=9)
+    print(f"case o_only {dtype} d_qk={dqk} flags={flags}", flush=True)
+    o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), dtype, flags=flags)
+    o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], d_scales=ex["scales"], flags=flags, return_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and lse is not None
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16))
+
+
 def test_host_and_device_scales_agree_bitwise():
     w = Workload("scales", 1, 260, 4, 2, 128, 128, "fp8", "gauss")
     q, k, v = make_inputs(w, seed=5)
