@@ -83,6 +83,9 @@ SMALL = [
     Workload("mla_group3_fp8", 1, 600, 6, 2, 192, 128, "fp8", "mla"),
     Workload("xcd_order_group3_fp8", 1, 300, 24, 8, 128, 128, "fp8", "gauss"),
     Workload("xcd_order_group3_bf16", 1, 300, 24, 8, 128, 128, "bf16", "outlier"),
+    # many short sequences: 64 x 130 tokens, a full and a 2-row query tile each
+    Workload("batch64_short_fp8", 64, 130, 4, 2, 128, 128, "fp8", "gauss"),
+    Workload("batch64_short_mla_bf16", 64, 130, 2, 2, 192, 128, "bf16", "mla"),
 ]
 
 
