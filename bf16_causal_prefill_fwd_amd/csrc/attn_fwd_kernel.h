@@ -10,9 +10,9 @@
 //  * One workgroup = 4 waves = 128 query rows of one (batch, head); each
 //    wave owns 32 rows and keeps its Q fragment in registers. Two workgroups
 //    share a CU, so each SIMD runs two independent waves. (BF16 at d = 128
-//    on long sequences: one workgroup of 8 waves = 256 rows per CU, which
-//    halves the staging traffic per FLOP; the two waves of a SIMD then share
-//    a barrier.)
+//    and FP8 at d_qk = 192 on long sequences: one workgroup of 8 waves = 256
+//    rows per CU, which halves the staging traffic per FLOP; the two waves
+//    of a SIMD then share a barrier.)
 //  * Software pipeline inside each wave, one key tile of BN keys per step
 //    (64 for FP8, 32 for BF16): while the softmax of tile n runs on the vector ALU, the same wave
 //    issues the MFMAs of S^T = K.Q^T for tile n+1 and of O^T += V^T.P^T for
@@ -103,17 +103,24 @@ struct FwdCfg {
   static constexpr int PV_STEPS = FP8 ? BN / 64 : BN / 16;   // key steps of one P.V output tile
   static constexpr int NPV = NOT * PV_STEPS;                 // P.V MFMAs per step
   static constexpr int NQK = NST * QK_STEPS;                 // Q.K^T MFMAs per step
-  static constexpr int KLOADS = KTILE / 16 / NTHREADS;       // 16-byte loads per lane per tile
+  // 16-byte loads per lane per tile; a K tile that does not split evenly
+  // over the workgroup (FP8 d_qk = 192 in 8 waves: 12 KiB over 8 KiB per
+  // instruction) has a last instruction that only the first waves need: the
+  // others load one line into a pad of their own, so every wave issues the
+  // same loads and the vmcnt bookkeeping stays one constant
+  static constexpr int KLOADS = (KTILE + 16 * NTHREADS - 1) / (16 * NTHREADS);
+  static constexpr bool KPART = KTILE % (16 * NTHREADS) != 0;
+  static constexpr int PAD_BYTES = KPART ? NWAVES * 1024 : 0;
   static constexpr int VLOADS = VTILE / 16 / NTHREADS;
   // loads a wave may leave in flight at the end of a step
   static constexpr int INFLIGHT = (NSTAGE - 2) * (KLOADS + VLOADS);
   static_assert((FP8 ? BN == 64 : (BN == 32 || BN == 64)), "FP8: 64 keys per step (one P operand); BF16: 32 or 64");
   static_assert(DV % 32 == 0 && DQK % 64 == 0, "head dims");
-  static_assert(KTILE % (16 * NTHREADS) == 0 && VTILE % (16 * NTHREADS) == 0, "staging split");
+  static_assert(KTILE % 1024 == 0 && VTILE % (16 * NTHREADS) == 0, "staging split");
   static_assert(NSTAGE >= 2 && INFLIGHT < 64, "ring depth / vmcnt range");
   static_assert(!STAGE_UNROLL || NSTAGE % 2 == 0, "the stage index must carry the score parity");
   static_assert(NWAVES == 4 || NWAVES == 8, "two waves per SIMD");
-  static_assert(WG_PER_CU * LDS_BYTES <= 160 * 1024, "LDS of the workgroups of one CU");
+  static_assert(WG_PER_CU * (LDS_BYTES + PAD_BYTES) <= 160 * 1024, "LDS of the workgroups of one CU");
 };
 
 // LDS swizzles: physical 16-byte chunk of logical chunk c in tile row r.
@@ -369,8 +376,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   for (int i = 0; i < C::KLOADS; ++i) {
     const int o = (i * C::NWAVES + wave) * 1024 + 16 * lane;
     const int row = o / C::KROW;
-    k_loff[i] = row * k_stride32 + 16 * k_swz<C::KCH>((o % C::KROW) / 16, row);
+    k_loff[i] = o < C::KTILE ? row * k_stride32 + 16 * k_swz<C::KCH>((o % C::KROW) / 16, row) : 0;
   }
+  // this wave's last K instruction past the tile: row 0 into its pad (after the K ring)
+  const bool k_pad = C::KPART && ((C::KLOADS - 1) * C::NWAVES + wave) * 1024 >= C::KTILE;
+  const uint32_t k_pad_addr = k_lds_addr + C::NSTAGE * C::KTILE + wave * 1024;
 #pragma unroll
   for (int i = 0; i < C::VLOADS; ++i) {
     const int o = (i * C::NWAVES + wave) * 1024 + 16 * lane;
@@ -391,26 +401,34 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   // tiles are all full and inside the sequence, one after the other: they
   // take the tile from a running pointer (`next`, advanced by one tile per
   // call) rather than from n.
+  // (pad_last: this wave's last instruction goes to its pad)
   auto issue_tile = [&](const uint8_t* base, int tile_bytes, int stride, const int* loff, int nloads, int rowbytes,
-                        uint32_t dst, int n, auto CHECKc, const uint8_t*& next) {
+                        uint32_t dst, int n, auto CHECKc, const uint8_t*& next, bool pad_last) {
+    auto dst_of = [&](int i) -> uint32_t {
+      return (i == nloads - 1 && pad_last) ? k_pad_addr : dst + i * C::NWAVES * 1024;
+    };
     if constexpr (!decltype(CHECKc)::value) {
       const uint8_t* tb = next;
       next += tile_bytes;
 #pragma unroll
-      for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst + i * C::NWAVES * 1024);
+      for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst_of(i));
       return;
     }
     const int nn = min(n, T - 1);
     const uint8_t* tb = base + (int64_t)nn * tile_bytes;
     if (nn < T_full) {
 #pragma unroll
-      for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst + i * C::NWAVES * 1024);
+      for (int i = 0; i < nloads; ++i) global_to_lds_16_async(tb, loff[i], dst_of(i));
     } else {
 #pragma unroll
       for (int i = 0; i < nloads; ++i) {
-        const int row = ((i * C::NWAVES + wave) * 1024 + 16 * lane) / rowbytes;
-        const int key = min(nn * BN + row, S - 1);
-        global_to_lds_16_async(tb, loff[i] + (key - nn * BN - row) * stride, dst + i * C::NWAVES * 1024);
+        if (i == nloads - 1 && pad_last) {
+          global_to_lds_16_async(tb, 0, k_pad_addr);  // row 0 of the tile: inside the sequence
+        } else {
+          const int row = ((i * C::NWAVES + wave) * 1024 + 16 * lane) / rowbytes;
+          const int key = min(nn * BN + row, S - 1);
+          global_to_lds_16_async(tb, loff[i] + (key - nn * BN - row) * stride, dst + i * C::NWAVES * 1024);
+        }
       }
     }
   };
@@ -419,11 +437,11 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
   const uint8_t* v_next = vbase;
   auto issue_k = [&](int n, int stage, auto CHECKc) {
     issue_tile(kbase, k_tile_bytes, k_stride32, k_loff, C::KLOADS, C::KROW, k_lds_w + stage * C::KTILE, n, CHECKc,
-               k_next);
+               k_next, k_pad);
   };
   auto issue_v = [&](int n, int stage, auto CHECKc) {
     issue_tile(vbase, v_tile_bytes, v_stride32, v_loff, C::VLOADS, C::VROW, v_lds_w + stage * C::VTILE, n, CHECKc,
-               v_next);
+               v_next, false);
   };
 
   // ---- per-lane LDS read offsets within a stage (the swizzle term depends
@@ -957,7 +975,7 @@ __device__ __forceinline__ void attn_fwd_body(const FwdParams& p, char* k_ring, 
 
 template <class C, int PM>
 __global__ __launch_bounds__(C::NTHREADS, C::WG_PER_CU) void attn_fwd_kernel(FwdParams p) {
-  __shared__ __attribute__((aligned(1024))) char k_ring[C::NSTAGE * C::KTILE];
+  __shared__ __attribute__((aligned(1024))) char k_ring[C::NSTAGE * C::KTILE + C::PAD_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_ring[C::NSTAGE * C::VTILE];
   float qs = p.q_scale, ks = p.k_scale, vs = p.v_scale;
   if (p.d_scales) {

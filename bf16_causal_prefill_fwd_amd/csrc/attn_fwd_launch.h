@@ -11,6 +11,11 @@ using CfgF8D128 = FwdCfg<true, 128, 128, 64, 4>;
 // registers of two waves per SIMD only with one MFMA job's operand reads in
 // flight instead of two)
 using CfgF8D192 = FwdCfg<true, 192, 128, 64, 4, true, 1>;
+// FP8 d_qk = 192 with exact P in 8-wave workgroups, under the same switch as
+// BF16 below: 1.0-1.5% faster on the 16K MLA layer on two boxes, outputs
+// bitwise identical (its 12 KiB K tile takes one and a half load
+// instructions per lane; FP8 d = 128 loses in 8 waves, 0.2-1.8%)
+using CfgF8D192W8 = FwdCfg<true, 192, 128, 64, 4, true, 1, 8>;
 using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4>;
 // BF16 d_qk = 128 in 8-wave workgroups (256 query rows, one per CU): half
 // the K/V staging per FLOP. Measured 1.5-1.9% faster than two 4-wave ones on
@@ -51,12 +56,14 @@ inline LaunchStatus launch_attn_fwd(FwdParams prm, bool fp8, int d_qk, int pmode
                        : launch_fwd<CfgF8D192, kPBlockScaledRoundedSum>(prm, stream);
   if (fp8 && pmode == kPLean)
     return d_qk == 128 ? launch_fwd<CfgF8D128, kPLean>(prm, stream) : launch_fwd<CfgF8D192, kPLean>(prm, stream);
-  if (fp8)
-    return d_qk == 128 ? launch_fwd<CfgF8D128, kPExact>(prm, stream) : launch_fwd<CfgF8D192, kPExact>(prm, stream);
+  // 8-wave workgroups (256 query rows) from kWave8MinSeq tokens when that
+  // grid has at least kWave8MinWorkgroups of them
+  const int64_t wg8 = (int64_t)prm.B * prm.Hq * ((prm.S + 255) / 256);
+  const bool wave8 = prm.S >= kWave8MinSeq && wg8 >= kWave8MinWorkgroups;
+  if (fp8 && d_qk == 128) return launch_fwd<CfgF8D128, kPExact>(prm, stream);
+  if (fp8) return wave8 ? launch_fwd<CfgF8D192W8, kPExact>(prm, stream) : launch_fwd<CfgF8D192, kPExact>(prm, stream);
   if (d_qk == 192) return launch_fwd<CfgBFD192, kPExact>(prm, stream);
-  const int64_t wg8 = (int64_t)prm.B * prm.Hq * ((prm.S + CfgBFD128W8::BM - 1) / CfgBFD128W8::BM);
-  return prm.S >= kWave8MinSeq && wg8 >= kWave8MinWorkgroups ? launch_fwd<CfgBFD128W8, kPExact>(prm, stream)
-                                                            : launch_fwd<CfgBFD128, kPExact>(prm, stream);
+  return wave8 ? launch_fwd<CfgBFD128W8, kPExact>(prm, stream) : launch_fwd<CfgBFD128, kPExact>(prm, stream);
 }
 
 }  // namespace attn

@@ -124,9 +124,11 @@ ZERO_Q = [
     (1, 300, 2, 2, 128),
     (2, 1087, 16, 4, 128),
     (2, 1087, 16, 4, 192),
-    # a grid large enough for BF16's 8-wave workgroups (33 x 32 >= 1,024 of
-    # them), ragged: the last 256-row tile holds 77 rows
+    # a grid large enough for 8-wave workgroups (33 x 32 >= 1,024 of them:
+    # BF16 at d = 128, FP8 at d_qk = 192), ragged: the last 256-row tile
+    # holds 77 rows
     (1, 8269, 32, 8, 128),
+    (1, 8269, 32, 8, 192),
 ]
 
 
@@ -226,58 +228,60 @@ def sample_rows(w: Workload, rng: np.random.Generator, n_heads: int = 6):
     return rows
 
 
-# BF16 d = 128 runs 8-wave workgroups (256 query rows) from 8,192 tokens when
-# that grid has at least 1,024 of them, 4-wave ones otherwise: these lengths
-# with 32 query heads are past the switch (33 to 34 tiles of 256 rows per head)
-# and put every ragged tail of a 256-row tile and of a 32-key step through the
-# 8-wave kernel
-EIGHT_WAVE_S = [8193, 8223, 8225, 8447, 8640]
+# BF16 d = 128 and FP8 d_qk = 192 (exact P) run 8-wave workgroups (256 query
+# rows) from 8,192 tokens when that grid has at least 1,024 of them, 4-wave
+# ones otherwise: these lengths with 32 query heads are past the switch (33
+# to 34 tiles of 256 rows per head) and put every ragged tail of a 256-row
+# tile and of a key step through the 8-wave kernels (FP8 d_qk = 192: a K
+# tile of one and a half load instructions per lane)
+EIGHT_WAVE_S = [8193, 8223, 8225, 8257, 8447, 8640]
+EIGHT_WAVE_KINDS = [("bf16", 128, True, "gauss"), ("fp8", 192, True, "mla"), ("fp8", 192, False, "mla")]
 
 
-@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
-def test_bf16_eight_wave_workgroups_sampled_rows(causal):
-    worst = (0.0, 0.0)
-    for S in EIGHT_WAVE_S if causal else EIGHT_WAVE_S[-1:]:
-        w = Workload(f"bf16_w8_{S}", 1, S, 32, 8, 128, 128, "bf16", "gauss", causal=causal)
-        assert S >= 8192 and w.B * w.Hq * -(-S // 256) >= 1024
-        q, k, v, o, lse, ex = run_case(w, seed=S)
-        rows = sample_rows(w, np.random.default_rng(S), n_heads=4)
-        ref = prefill_reference(q, k, v, "bf16", causal=causal, rows=rows)
-        bi = torch.tensor([r[0] for r in rows]); hi = torch.tensor([r[1] for r in rows])
-        ii = torch.tensor([r[2] for r in rows])
-        og = o[bi, ii, hi].float().cpu().numpy().astype(np.float64)
-        lg = lse[bi, hi, ii].cpu().numpy().astype(np.float64)
-        err, _ = check_o(og, ref["o_rows"], "bf16", f"S={S} {len(rows)} rows: ")
-        lerr = float(np.max(np.abs(lg - ref["lse_rows"])))
-        assert lerr <= LSE_TOL, (S, lerr)
-        worst = (max(worst[0], err), max(worst[1], lerr))
-        o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], causal=causal)
-        assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(l2, lse)
-    print(f"  worst: O rel-L2 {worst[0]:.3e}  LSE max-abs {worst[1]:.3e}", flush=True)
-
-
-# the 8-wave BF16 kernel under both work orders: two sequences with B * Hkv = 8
-# (whole kv units per XCD) and G = 6 query heads per kv head with B * Hkv = 6
-# (plain tile-major order)
-EIGHT_WAVE_ORDERS = [Workload("bf16_w8_batch2_xcd_order", 2, 8200, 16, 4, 128, 128, "bf16", "gauss"),
-                     Workload("bf16_w8_group6_plain_order", 1, 8300, 36, 6, 128, 128, "bf16", "outlier")]
-
-
-@pytest.mark.parametrize("w", EIGHT_WAVE_ORDERS, ids=[w.name for w in EIGHT_WAVE_ORDERS])
-def test_bf16_eight_wave_work_orders_sampled_rows(w):
-    assert w.S >= 8192 and w.B * w.Hq * -(-w.S // 256) >= 1024
-    q, k, v, o, lse, ex = run_case(w, seed=w.S)
-    rows = sample_rows(w, np.random.default_rng(w.S), n_heads=4)
-    assert len({r[0] for r in rows}) == w.B
-    ref = prefill_reference(q, k, v, "bf16", rows=rows)
+def _sampled_rows_check(w, seed, fold_q, n_heads=4):
+    q, k, v, o, lse, ex = run_case(w, seed=seed, fold_q=fold_q)
+    rows = sample_rows(w, np.random.default_rng(seed), n_heads=n_heads)
+    ref = prefill_reference(q, k, v, w.dtype, causal=w.causal, rows=rows, fold_q=fold_q)
     bi = torch.tensor([r[0] for r in rows]); hi = torch.tensor([r[1] for r in rows])
     ii = torch.tensor([r[2] for r in rows])
     og = o[bi, ii, hi].float().cpu().numpy().astype(np.float64)
     lg = lse[bi, hi, ii].cpu().numpy().astype(np.float64)
-    check_o(og, ref["o_rows"], "bf16", f"{len(rows)} rows: ")
+    err, _ = check_o(og, ref["o_rows"], w.dtype, f"S={w.S} {len(rows)} rows: ")
     lerr = float(np.max(np.abs(lg - ref["lse_rows"])))
     print(f"  LSE max-abs {lerr:.3e}", flush=True)
-    assert lerr <= LSE_TOL
+    assert lerr <= LSE_TOL, (w.S, lerr)
+    o2, l2 = ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], causal=w.causal, d_scales=ex["scales"])
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16)) and torch.equal(l2, lse)
+    return rows, err, lerr
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+@pytest.mark.parametrize("dtype,dqk,fold_q,dist", EIGHT_WAVE_KINDS,
+                         ids=[f"{t}_d{d}" + ("" if f else "_plain_q") for t, d, f, _ in EIGHT_WAVE_KINDS])
+def test_eight_wave_workgroups_sampled_rows(dtype, dqk, fold_q, dist, causal):
+    worst = (0.0, 0.0)
+    for S in EIGHT_WAVE_S if causal else EIGHT_WAVE_S[-1:]:
+        w = Workload(f"{dtype}_d{dqk}_w8_{S}", 1, S, 32, 8, dqk, 128, dtype, dist, causal=causal)
+        assert S >= 8192 and w.B * w.Hq * -(-S // 256) >= 1024
+        _, err, lerr = _sampled_rows_check(w, S, fold_q)
+        worst = (max(worst[0], err), max(worst[1], lerr))
+    print(f"  worst: O rel-L2 {worst[0]:.3e}  LSE max-abs {worst[1]:.3e}", flush=True)
+
+
+# the 8-wave kernels under both work orders: two sequences with B * Hkv = 8
+# (whole kv units per XCD) and G = 6 query heads per kv head with B * Hkv = 6
+# (plain tile-major order)
+EIGHT_WAVE_ORDERS = [Workload("bf16_w8_batch2_xcd_order", 2, 8200, 16, 4, 128, 128, "bf16", "gauss"),
+                     Workload("bf16_w8_group6_plain_order", 1, 8300, 36, 6, 128, 128, "bf16", "outlier"),
+                     Workload("fp8_mla_w8_batch2_xcd_order", 2, 8200, 16, 4, 192, 128, "fp8", "mla"),
+                     Workload("fp8_mla_w8_group6_plain_order", 1, 8300, 36, 6, 192, 128, "fp8", "mla")]
+
+
+@pytest.mark.parametrize("w", EIGHT_WAVE_ORDERS, ids=[w.name for w in EIGHT_WAVE_ORDERS])
+def test_eight_wave_work_orders_sampled_rows(w):
+    assert w.S >= 8192 and w.B * w.Hq * -(-w.S // 256) >= 1024
+    rows, _, _ = _sampled_rows_check(w, w.S, True)
+    assert len({r[0] for r in rows}) == w.B
 
 
 # every workload with the pipeline's folded query scale; the FP8 layers also
