@@ -9,13 +9,19 @@ Q.K^T, online softmax, P.V, O and LSE epilogue). The default workload is the
 long-context headline shape: B=1, S=32768, H=32, d=128, causal, FP8 e4m3
 with per-tensor scales, Q, K, V ~ N(0, 1).
 
+FP8 input step: by default Q and K are rotated by Hadamard blocks before the
+per-tensor cast (attn_quantize_fp8_qkv_hadamard), which keeps the LSE within
+its bar on heavy-tailed activations; ``--no-hadamard`` takes the unrotated
+step (attn_quantize_fp8_qkv). The attention kernel is the same either way.
+
 Prints ONE JSON line. ``value`` is the algorithmic causal FLOP count
 B*Hq*S^2*(d_qk+d_v) divided by the measured time of a whole step, in TFLOP/s.
 The attention kernel alone is reported beside it and in ``roofline``, whose
 duration comes from HIP events recorded on the stream the kernel runs on.
 For FP8, the input step folds Q's scale so that the score factor is a power
-of two; ``attention_plain_q_scale`` times the same attention with Q under its
-plain per-tensor absmax scale (the kernel's fma form) beside it.
+of two; ``attention_plain_q_scale`` times the same attention on the literal
+per-tensor step (Q and K unrotated under their plain absmax scales, the
+kernel's fma form) beside it.
 ``cpu_baseline`` times the fp64 CPU oracle on the first four query heads of
 batch 0 of the same workload (all S query rows each), on this host's cores.
 
@@ -181,15 +187,17 @@ def sustained(seconds: float, attention, flops: float, stream, peak_tflops: floa
     return rec
 
 
-def plain_q_scale_leg(steps: int, w, q32, codes, scales, o, flags: int, flops: float, peak: float, sm_scale: float,
-                      stream) -> dict:
-    """The FP8 attention again, with Q under its plain per-tensor absmax scale.
+def plain_q_scale_leg(steps: int, w, q32, k32, codes, scales, o, flags: int, flops: float, peak: float,
+                      sm_scale: float, stream) -> dict:
+    """The FP8 attention again, on the literal per-tensor input step: Q and K
+    unrotated, under their plain absmax scales.
 
-    The input step folds Q's scale so that the score factor q_scale * k_scale
-    * softmax_scale * log2(e) is a power of two, which lets the kernel apply
-    it through the MFMA operand scales. With the plain scale the factor is
-    generally not a power of two and the kernel applies it with one fma per
-    score. Same K, V codes and scales; own Q codes, O and LSE buffers.
+    The default input step rotates Q and K and folds Q's scale so that the
+    score factor q_scale * k_scale * softmax_scale * log2(e) is a power of
+    two, which lets the kernel apply it through the MFMA operand scales. With
+    the plain scales the factor is generally not a power of two and the
+    kernel applies it with one fma per score. Same V codes and scale; own Q
+    and K codes, O and LSE buffers.
     """
     import numpy as np
     import torch
@@ -198,14 +206,16 @@ def plain_q_scale_leg(steps: int, w, q32, codes, scales, o, flags: int, flops: f
 
     print(f"# plain absmax Q scale: {steps} attention launches", file=sys.stderr, flush=True)
     q_plain = torch.empty_like(codes[0])
+    k_plain = torch.empty_like(codes[1])
     scales_plain = torch.empty(3, dtype=torch.float32, device=q32.device)
     ops.attn_quantize_fp8(q32, out=q_plain, scale=scales_plain[0:1], stream=stream)
-    scales_plain[1:].copy_(scales[1:])
+    ops.attn_quantize_fp8(k32, out=k_plain, scale=scales_plain[1:2], stream=stream)
+    scales_plain[2:].copy_(scales[2:])
     o_plain = torch.empty_like(o)
     lse_plain = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=q32.device)
 
     def run():
-        ops.attn_prefill_fwd(q_plain, codes[1], codes[2], causal=w.causal, out=o_plain, lse=lse_plain,
+        ops.attn_prefill_fwd(q_plain, k_plain, codes[2], causal=w.causal, out=o_plain, lse=lse_plain,
                              d_scales=scales_plain, stream=stream, flags=flags)
 
     for _ in range(3):
@@ -230,8 +240,8 @@ def plain_q_scale_leg(steps: int, w, q32, codes, scales, o, flags: int, flops: f
         "attention_ms_min": round(float(np.min(ms)), 4),
         "attention_tflops": round(tflops, 2),
         "attention_frac_of_peak": round(tflops / peak, 4),
-        "note": "Q quantized with its plain absmax/448 scale (attn_quantize_fp8); the headline uses the folded "
-                "query scale of attn_quantize_fp8_qkv",
+        "note": "Q and K unrotated under their plain absmax/448 scales (attn_quantize_fp8), the literal "
+                "per-tensor input step; the headline's input step rotates Q and K and folds Q's scale",
     }
 
 
@@ -298,7 +308,7 @@ def cpu_baseline(w, q, k, v, n_heads: int = 4, hadamard: bool = False, o_gpu=Non
     tq, tk, tv = make_inputs("tiny_mha_fp8", seed=0)
     with threadpool_limits(limits=1):
         t1 = time.perf_counter()
-        prefill_reference(tq, tk, tv, "fp8", fold_q=True)
+        prefill_reference(tq, tk, tv, "fp8", fold_q=True, hadamard=True)
         t1 = time.perf_counter() - t1
     tiny_flops = 2 * 512 ** 2 * 256
     rec["tiny_one_thread"] = {"workload": "tiny_mha_fp8 (B=1, S=512, H=2, d=128, FP8)", "seconds": round(t1, 3),
@@ -313,8 +323,11 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--hadamard", action="store_true",
-                    help="FP8: rotate Q and K by Hadamard blocks in the input step (attn_quantize_fp8_qkv_hadamard)")
+    ap.add_argument("--hadamard", dest="hadamard", action="store_true", default=None,
+                    help="FP8: rotate Q and K by Hadamard blocks in the input step "
+                         "(attn_quantize_fp8_qkv_hadamard; the default for FP8 workloads)")
+    ap.add_argument("--no-hadamard", dest="hadamard", action="store_false",
+                    help="FP8: the unrotated input step (attn_quantize_fp8_qkv)")
     ap.add_argument("--p-block-scale", action="store_true",
                     help="FP8: per (row, 64-key block) power-of-two scaling of P (ATTN_FLAG_P_BLOCK_SCALE)")
     ap.add_argument("--p-rounded-sum", action="store_true",
@@ -392,6 +405,8 @@ def main(argv=None) -> int:
     if (args.hadamard or args.p_block_scale or args.p_rounded_sum) and w.dtype != "fp8":
         print("--hadamard, --p-block-scale and --p-rounded-sum apply to FP8 workloads only", file=sys.stderr)
         return 2
+    if args.hadamard is None:
+        args.hadamard = w.dtype == "fp8"
     flags = (ops.ATTN_FLAG_P_BLOCK_SCALE if args.p_block_scale else 0) | \
         (ops.ATTN_FLAG_P_ROUNDED_SUM if args.p_rounded_sum else 0)
 
@@ -502,9 +517,9 @@ def main(argv=None) -> int:
     else:
         rec["sustained"] = None
     rec["attention_plain_q_scale"] = None
-    if w.dtype == "fp8" and not args.hadamard and not args.no_plain_q_scale:
-        rec["attention_plain_q_scale"] = plain_q_scale_leg(args.steps, w, q32, codes, scales, o, flags, flops, peak,
-                                                           sm_scale, stream)
+    if w.dtype == "fp8" and not args.no_plain_q_scale:
+        rec["attention_plain_q_scale"] = plain_q_scale_leg(args.steps, w, q32, k32, codes, scales, o, flags, flops,
+                                                           peak, sm_scale, stream)
     if not args.no_cpu_baseline:
         print("# cpu baseline (fp64 oracle, four head slices)", file=sys.stderr, flush=True)
         nh = min(4, w.Hq)

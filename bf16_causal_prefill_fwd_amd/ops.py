@@ -369,18 +369,28 @@ def attn_prefill(q, k, v, q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True):
 
 
 def prefill(q32: torch.Tensor, k32: torch.Tensor, v32: torch.Tensor, dtype: str = "fp8", causal=True,
-            stream=None, fold_q: bool = True, hadamard: bool = False, flags: int = 0):
+            stream=None, fold_q: bool = True, hadamard: bool | None = None, flags: int = 0):
     """The whole path on float32 device inputs: input step, then attention.
 
     dtype "fp8": per-tensor quantization (scales stay on the device and are
-    read by the kernel, so no host synchronisation); with ``fold_q`` the query
-    takes the folded scale (see attn_quantize_fp8). With ``hadamard`` (fp8
-    only; implies ``fold_q``) Q and K are rotated before the cast.
+    read by the kernel, so no host synchronisation). By default Q and K are
+    rotated by Hadamard blocks before the cast and the query takes the folded
+    scale (attn_quantize_fp8_qkv_hadamard): on heavy-tailed activations the
+    rotation spreads outlier channels over the head dim, which keeps the FP8
+    matrix core's summing error on a row's largest scores, and so the LSE,
+    within its bar (aicronaca.it, "Perché l'FP8 non basta da solo"). With
+    ``hadamard=False`` the unrotated tensors are quantized, with the folded
+    query scale when ``fold_q``; ``fold_q=False`` gives the plain per-tensor
+    absmax scales (no rotation: it implies the folded query scale).
     "bf16": RNE cast. ``flags`` (ATTN_FLAG_* bits) go to the attention call.
     Returns (o, lse, extras) where extras holds the codes and the scale tensor.
     """
+    if hadamard is None:
+        hadamard = dtype == "fp8" and fold_q
     if hadamard and dtype != "fp8":
         raise ValueError("the Hadamard rotation applies to the fp8 path")
+    if hadamard and not fold_q:
+        raise ValueError("the rotated input step folds the query scale: hadamard needs fold_q")
     if dtype == "fp8" and (fold_q or hadamard):
         (q8, k8, v8), scales = attn_quantize_fp8_qkv(q32, k32, v32, 1.0 / math.sqrt(q32.shape[-1]), stream=stream,
                                                      hadamard=hadamard)

@@ -47,7 +47,7 @@ GATE_FULL = ["gqa_fp8_outlier_16k", "mha_fp8_32k", "mla_fp8_16k"]
 
 
 def _lean(q, k, v, causal=True):
-    o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), "fp8", causal=causal, flags=LEAN)
+    o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), "fp8", causal=causal, hadamard=False, flags=LEAN)
     torch.cuda.synchronize()
     assert lse is None
     return o, ex
@@ -101,7 +101,7 @@ def test_lean_p_zero_query_closed_form():
 def test_lean_p_rejects_lse_and_bf16():
     w = Workload("x", 1, 64, 2, 2, 128, 128, "fp8", "gauss")
     q, k, v = make_inputs(w, seed=1)
-    _, _, ex = ops.prefill(dev(q), dev(k), dev(v), "fp8")
+    _, _, ex = ops.prefill(dev(q), dev(k), dev(v), "fp8", hadamard=False)
     lse = torch.empty((1, 2, 64), dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
         ops.attn_prefill_fwd(ex["q"], ex["k"], ex["v"], d_scales=ex["scales"], flags=LEAN, lse=lse)

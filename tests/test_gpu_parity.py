@@ -38,10 +38,16 @@ def codes_np(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
+def rot(dtype: str, fold_q: bool) -> bool:
+    """Whether the pipeline's default FP8 input step rotates Q and K: it does
+    with the folded query scale; the plain-scale step is the unrotated one."""
+    return dtype == "fp8" and fold_q
+
+
 def run_case(w: Workload, seed: int, fold_q: bool = True):
     q, k, v = make_inputs(w, seed)
     print(f"case {w.name} B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d_qk}/{w.d_v} {w.dtype} "
-          f"causal={w.causal} seed={seed} fold_q={fold_q}", flush=True)
+          f"causal={w.causal} seed={seed} fold_q={fold_q} rotated={rot(w.dtype, fold_q)}", flush=True)
     o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), w.dtype, causal=w.causal, fold_q=fold_q)
     torch.cuda.synchronize()
     return q, k, v, o, lse, ex
@@ -98,7 +104,7 @@ SMALL_RUNS = [(w, True) for w in SMALL] + [(w, False) for w in SMALL if w.dtype 
                          ids=[w.name + ("" if f else "_plain_q") for w, f in SMALL_RUNS])
 def test_small_full_oracle(w, fold_q):
     q, k, v, o, lse, ex = run_case(w, seed=1, fold_q=fold_q)
-    ref = prefill_reference(q, k, v, w.dtype, causal=w.causal, fold_q=fold_q)
+    ref = prefill_reference(q, k, v, w.dtype, causal=w.causal, fold_q=fold_q, hadamard=rot(w.dtype, fold_q))
     for name in ("q", "k", "v"):
         assert np.array_equal(codes_np(ex[name]), ref[name + "_codes"]), f"{name} codes differ"
     if w.dtype == "fp8":
@@ -241,7 +247,8 @@ EIGHT_WAVE_KINDS = [("bf16", 128, True, "gauss"), ("fp8", 192, True, "mla"), ("f
 def _sampled_rows_check(w, seed, fold_q, n_heads=4):
     q, k, v, o, lse, ex = run_case(w, seed=seed, fold_q=fold_q)
     rows = sample_rows(w, np.random.default_rng(seed), n_heads=n_heads)
-    ref = prefill_reference(q, k, v, w.dtype, causal=w.causal, rows=rows, fold_q=fold_q)
+    ref = prefill_reference(q, k, v, w.dtype, causal=w.causal, rows=rows, fold_q=fold_q,
+                            hadamard=rot(w.dtype, fold_q))
     bi = torch.tensor([r[0] for r in rows]); hi = torch.tensor([r[1] for r in rows])
     ii = torch.tensor([r[2] for r in rows])
     og = o[bi, ii, hi].float().cpu().numpy().astype(np.float64)
@@ -296,7 +303,7 @@ def test_full_size_sampled_rows(name, fold_q):
     q, k, v, o, lse, ex = run_case(w, seed=0, fold_q=fold_q)
     rng = np.random.default_rng(12345)
     rows = sample_rows(w, rng)
-    ref = prefill_reference(q, k, v, w.dtype, rows=rows, fold_q=fold_q)
+    ref = prefill_reference(q, k, v, w.dtype, rows=rows, fold_q=fold_q, hadamard=rot(w.dtype, fold_q))
     if w.dtype == "fp8":
         sc = ex["scales"].cpu().numpy()
         assert np.array_equal(sc, np.float32([ref["q_scale"], ref["k_scale"], ref["v_scale"]]))
@@ -345,7 +352,7 @@ def test_sequence_lengths_around_tile_boundaries(dtype, fold_q):
     for S in BOUNDARY_S:
         w = Workload(f"boundary_{S}", 1, S, 4, 2, 128, 128, dtype, "gauss")
         q, k, v, o, lse, ex = run_case(w, seed=S, fold_q=fold_q)
-        ref = prefill_reference(q, k, v, dtype, fold_q=fold_q)
+        ref = prefill_reference(q, k, v, dtype, fold_q=fold_q, hadamard=rot(dtype, fold_q))
         err, row = check_o(o.float().cpu().numpy().astype(np.float64), ref["o"], dtype, f"S={S}: ")
         lerr = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref["lse"])))
         worst = (max(worst[0], err), max(worst[1], row), max(worst[2], lerr))
@@ -361,7 +368,7 @@ def test_noncausal_through_the_unchecked_loop(dtype):
     for S in (577, 705, 1087):
         w = Workload(f"noncausal_{S}", 1, S, 4, 2, 128, 128, dtype, "gauss", causal=False)
         q, k, v, o, lse, ex = run_case(w, seed=S)
-        ref = prefill_reference(q, k, v, dtype, causal=False, fold_q=True)
+        ref = prefill_reference(q, k, v, dtype, causal=False, fold_q=True, hadamard=rot(dtype, True))
         check_o(o.float().cpu().numpy().astype(np.float64), ref["o"], dtype, f"S={S}: ")
         lerr = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref["lse"])))
         print(f"  S={S}: LSE max-abs {lerr:.3e}", flush=True)
@@ -391,7 +398,7 @@ def test_running_max_grows_every_tile(dtype, dqk, fold_q):
     print(f"case rising scores {dtype} S={S} d_qk={dqk} fold_q={fold_q}", flush=True)
     o, lse, ex = ops.prefill(dev(q), dev(k), dev(v), dtype, fold_q=fold_q)
     torch.cuda.synchronize()
-    ref = prefill_reference(q, k, v, dtype, fold_q=fold_q)
+    ref = prefill_reference(q, k, v, dtype, fold_q=fold_q, hadamard=rot(dtype, fold_q))
     check_o(o.float().cpu().numpy().astype(np.float64), ref["o"], dtype)
     lerr = float(np.max(np.abs(lse.cpu().numpy().astype(np.float64) - ref["lse"])))
     print(f"  LSE max-abs {lerr:.3e}", flush=True)
@@ -408,7 +415,7 @@ def test_long_context_64k_sampled_rows():
     rng = np.random.default_rng(64)
     rows = [(0, int(h), int(i)) for h in (0, 7) for i in sorted(set([0, 1, 32767, 32768, 65534, 65535]
                                                                      + list(rng.integers(0, w.S, 4))))]
-    ref = prefill_reference(q, k, v, "fp8", rows=rows, fold_q=True)
+    ref = prefill_reference(q, k, v, "fp8", rows=rows, fold_q=True, hadamard=True)
     sc = ex["scales"].cpu().numpy()
     assert np.array_equal(sc, np.float32([ref["q_scale"], ref["k_scale"], ref["v_scale"]]))
     bi = torch.tensor([r[0] for r in rows]); hi = torch.tensor([r[1] for r in rows])

@@ -49,7 +49,7 @@ def test_small_block_scaled(w, fold_q):
     print(f"case {w.name} S={w.S} Hq={w.Hq} Hkv={w.Hkv} d={w.d_qk} causal={w.causal} fold_q={fold_q} "
           f"block-scaled P", flush=True)
     o, lse, ex = _run(q, k, v, w.causal, fold_q)
-    ref = prefill_reference(q, k, v, "fp8", causal=w.causal, fold_q=fold_q)
+    ref = prefill_reference(q, k, v, "fp8", causal=w.causal, fold_q=fold_q, hadamard=fold_q)
     for name in ("q", "k", "v"):
         assert np.array_equal(codes_np(ex[name]), ref[name + "_codes"])
     og = o.float().cpu().numpy().astype(np.float64)
@@ -104,7 +104,7 @@ def test_monotone_scores_block_scaled(rising, fold_q):
     q, k, v = _ramp_inputs(700, 2, rising, seed=21 if rising else 22)
     print(f"case {'rising' if rising else 'falling'} scores, block-scaled P, fold_q={fold_q}", flush=True)
     o, lse, ex = _run(q, k, v, fold_q=fold_q)
-    ref = prefill_reference(q, k, v, "fp8", fold_q=fold_q)
+    ref = prefill_reference(q, k, v, "fp8", fold_q=fold_q, hadamard=fold_q)
     err, _ = check_o(o.float().cpu().numpy().astype(np.float64), ref["o"], "fp8")
     lerr = _lse_err(lse, ref["lse"])
     o0, _, _ = _run(q, k, v, fold_q=fold_q, flags=0)
@@ -125,7 +125,7 @@ def test_full_size_block_scaled(name):
     print(f"case {name} full size, block-scaled P", flush=True)
     o, lse, ex = _run(q, k, v)
     rows = sample_rows(w, np.random.default_rng(12345))
-    ref = prefill_reference(q, k, v, "fp8", rows=rows, fold_q=True)
+    ref = prefill_reference(q, k, v, "fp8", rows=rows, fold_q=True, hadamard=True)
     bi = torch.tensor([r[0] for r in rows]); hi = torch.tensor([r[1] for r in rows])
     ii = torch.tensor([r[2] for r in rows])
     og = o[bi, ii, hi].float().cpu().numpy().astype(np.float64)
