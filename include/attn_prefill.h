@@ -234,7 +234,12 @@ int attn_quantize_fp8_hadamard(const void* x, int x_dtype, uint8_t* x8, float* d
  * for the rotated K's scale, its stored scale divided by the block size), V
  * plain, in one absmax launch and one encode launch over the three tensors
  * (aicronaca.it, "Perché l'FP8 non basta da solo": the rotation costs a
- * small fraction of the attention time). Arguments as attn_quantize_fp8_qkv,
+ * small fraction of the attention time). Use it on heavy-tailed
+ * activations: the FP8 matrix core sums a Q.K dot product only to about
+ * 2^-12 of its sum of |products|, so where large Q and K channels meet (logits
+ * of 50-80) the unrotated codes can move a row's LSE by up to ~2e-2; the
+ * rotation spreads those channels over every column (under 6e-4 on the same
+ * rows). Arguments as attn_quantize_fp8_qkv,
  * plus d, the head dim of Q and K (nq and nk multiples of it; blocks of
  * 64 or 128 columns as attn_quantize_fp8_hadamard, else
  * ATTN_ERR_UNSUPPORTED). The codes and scales equal those of the three
