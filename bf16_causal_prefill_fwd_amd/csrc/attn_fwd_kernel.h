@@ -9,12 +9,13 @@
 //
 //  * One workgroup = 4 waves = 128 query rows of one (batch, head); each
 //    wave owns 32 rows and keeps its Q fragment in registers. Two workgroups
-//    share a CU, so each SIMD runs two independent waves. (BF16 at d = 128
-//    and FP8 at d_qk = 192 on long sequences: one workgroup of 8 waves = 256
-//    rows per CU, which halves the staging traffic per FLOP; the two waves
-//    of a SIMD then share a barrier.)
+//    share a CU, so each SIMD runs two independent waves. (BF16, and FP8 at
+//    d_qk = 192, on long sequences: one workgroup of 8 waves = 256 rows per
+//    CU, which halves the staging traffic per FLOP; the two waves of a SIMD
+//    then share a barrier.)
 //  * Software pipeline inside each wave, one key tile of BN keys per step
-//    (64 for FP8, 32 for BF16): while the softmax of tile n runs on the vector ALU, the same wave
+//    (64 for FP8 and for 8-wave BF16 at d = 128, 32 for the other BF16
+//    forms): while the softmax of tile n runs on the vector ALU, the same wave
 //    issues the MFMAs of S^T = K.Q^T for tile n+1 and of O^T += V^T.P^T for
 //    tile n-1, interleaved with it in a fixed order, so both pipes stay busy
 //    without relying on another wave's phase (the pages overlap the two

@@ -24,11 +24,17 @@ using CfgBFD128 = FwdCfg<false, 128, 128, 32, 4>;
 // (every wave runs every step of its workgroup) outweighs the staging (+4%
 // at 4K, +18% at 1K and 512 tokens, however many sequences), and on small
 // grids (+39% at 1K tokens and 32 heads, B = 1). So it runs from 8K tokens,
-// when its grid has at least 4 workgroups per CU of the 256.
-using CfgBFD128W8 = FwdCfg<false, 128, 128, 32, 4, true, 2, 8>;
+// when its grid has at least 4 workgroups per CU of the 256. Its key step is
+// 64 keys (the 4-wave form spills with 64 and keeps 32): another 1.2-3.2%
+// from 8K to 64K tokens.
+using CfgBFD128W8 = FwdCfg<false, 128, 128, 64, 4, true, 2, 8>;
 constexpr int kWave8MinSeq = 8192;
 constexpr int64_t kWave8MinWorkgroups = 1024;
 using CfgBFD192 = FwdCfg<false, 192, 128, 32, 4>;
+// BF16 d_qk = 192 in 8-wave workgroups under the same switch: 2.0% faster at
+// 16K and 32K tokens (16 heads), 4.3% at 8K (32 heads), outputs bitwise
+// identical (64-key steps spill here)
+using CfgBFD192W8 = FwdCfg<false, 192, 128, 32, 4, true, 2, 8>;
 
 enum LaunchStatus { kLaunched = 0, kTooManyWorkgroups = 1, kLaunchFailed = 2 };
 
@@ -62,7 +68,7 @@ inline LaunchStatus launch_attn_fwd(FwdParams prm, bool fp8, int d_qk, int pmode
   const bool wave8 = prm.S >= kWave8MinSeq && wg8 >= kWave8MinWorkgroups;
   if (fp8 && d_qk == 128) return launch_fwd<CfgF8D128, kPExact>(prm, stream);
   if (fp8) return wave8 ? launch_fwd<CfgF8D192W8, kPExact>(prm, stream) : launch_fwd<CfgF8D192, kPExact>(prm, stream);
-  if (d_qk == 192) return launch_fwd<CfgBFD192, kPExact>(prm, stream);
+  if (d_qk == 192) return wave8 ? launch_fwd<CfgBFD192W8, kPExact>(prm, stream) : launch_fwd<CfgBFD192, kPExact>(prm, stream);
   return wave8 ? launch_fwd<CfgBFD128W8, kPExact>(prm, stream) : launch_fwd<CfgBFD128, kPExact>(prm, stream);
 }
 

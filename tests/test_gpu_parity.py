@@ -131,8 +131,8 @@ ZERO_Q = [
     (2, 1087, 16, 4, 128),
     (2, 1087, 16, 4, 192),
     # a grid large enough for 8-wave workgroups (33 x 32 >= 1,024 of them:
-    # BF16 at d = 128, FP8 at d_qk = 192), ragged: the last 256-row tile
-    # holds 77 rows
+    # BF16, and FP8 at d_qk = 192), ragged: the last 256-row tile holds 77
+    # rows
     (1, 8269, 32, 8, 128),
     (1, 8269, 32, 8, 192),
 ]
@@ -234,14 +234,15 @@ def sample_rows(w: Workload, rng: np.random.Generator, n_heads: int = 6):
     return rows
 
 
-# BF16 d = 128 and FP8 d_qk = 192 (exact P) run 8-wave workgroups (256 query
-# rows) from 8,192 tokens when that grid has at least 1,024 of them, 4-wave
-# ones otherwise: these lengths with 32 query heads are past the switch (33
-# to 34 tiles of 256 rows per head) and put every ragged tail of a 256-row
-# tile and of a key step through the 8-wave kernels (FP8 d_qk = 192: a K
-# tile of one and a half load instructions per lane)
+# BF16 and FP8 d_qk = 192 (exact P) run 8-wave workgroups (256 query rows)
+# from 8,192 tokens when that grid has at least 1,024 of them, 4-wave ones
+# otherwise: these lengths with 32 query heads are past the switch (33 to 34
+# tiles of 256 rows per head) and put every ragged tail of a 256-row tile and
+# of a key step (64 keys; 32 for BF16 d_qk = 192) through the 8-wave kernels
+# (d_qk = 192: a K tile of one and a half load instructions per lane)
 EIGHT_WAVE_S = [8193, 8223, 8225, 8257, 8447, 8640]
-EIGHT_WAVE_KINDS = [("bf16", 128, True, "gauss"), ("fp8", 192, True, "mla"), ("fp8", 192, False, "mla")]
+EIGHT_WAVE_KINDS = [("bf16", 128, True, "gauss"), ("bf16", 192, True, "mla"), ("fp8", 192, True, "mla"),
+                    ("fp8", 192, False, "mla")]
 
 
 def _sampled_rows_check(w, seed, fold_q, n_heads=4):
@@ -280,6 +281,7 @@ def test_eight_wave_workgroups_sampled_rows(dtype, dqk, fold_q, dist, causal):
 # (plain tile-major order)
 EIGHT_WAVE_ORDERS = [Workload("bf16_w8_batch2_xcd_order", 2, 8200, 16, 4, 128, 128, "bf16", "gauss"),
                      Workload("bf16_w8_group6_plain_order", 1, 8300, 36, 6, 128, 128, "bf16", "outlier"),
+                     Workload("bf16_mla_w8_batch2_xcd_order", 2, 8200, 16, 4, 192, 128, "bf16", "mla"),
                      Workload("fp8_mla_w8_batch2_xcd_order", 2, 8200, 16, 4, 192, 128, "fp8", "mla"),
                      Workload("fp8_mla_w8_group6_plain_order", 1, 8300, 36, 6, 192, 128, "fp8", "mla")]
 
