@@ -381,7 +381,7 @@ def prefill(q32: torch.Tensor, k32: torch.Tensor, v32: torch.Tensor, dtype: str 
     within its bar (aicronaca.it, "Perché l'FP8 non basta da solo"). With
     ``hadamard=False`` the unrotated tensors are quantized, with the folded
     query scale when ``fold_q``; ``fold_q=False`` gives the plain per-tensor
-    absmax scales (no rotation: it implies the folded query scale).
+    absmax scales, unrotated (the rotated step always folds the query scale).
     "bf16": RNE cast. ``flags`` (ATTN_FLAG_* bits) go to the attention call.
     Returns (o, lse, extras) where extras holds the codes and the scale tensor.
     """
