@@ -293,6 +293,40 @@ def test_eight_wave_work_orders_sampled_rows(w):
     assert len({r[0] for r in rows}) == w.B
 
 
+# seeded random shapes past the 8-wave switch: batch 1-2, 1-8 kv heads with
+# 1-8 query heads each, 8,192-9,299 tokens (any ragged tail), causal or not,
+# through every 8-wave kernel
+def _eight_wave_draw(n: int, seed: int = 31):
+    rng = np.random.default_rng(seed)
+    kinds = [("bf16", 128, True, "gauss"), ("bf16", 128, True, "outlier"), ("bf16", 192, True, "mla"),
+             ("fp8", 192, True, "mla"), ("fp8", 192, False, "mla")]
+    cases = []
+    for i in range(n):
+        dtype, dqk, fold_q, dist = kinds[int(rng.integers(len(kinds)))]
+        while True:
+            B, Hkv = int(rng.integers(1, 3)), int(rng.integers(1, 9))
+            G, S = int(rng.choice([1, 2, 3, 4, 6, 8])), int(rng.integers(8192, 9300))
+            if B * G * Hkv * -(-S // 256) >= 1024 and B * G * Hkv <= 64:
+                break
+        causal = bool(rng.random() < 0.8)
+        w = Workload(f"w8rand{i}_{dtype}_d{dqk}_B{B}_S{S}_G{G}x{Hkv}", B, S, G * Hkv, Hkv, dqk, 128, dtype, dist,
+                     causal=causal)
+        cases.append((w, fold_q, 5000 + i))
+    return cases
+
+
+EIGHT_WAVE_RANDOM = _eight_wave_draw(12)
+
+
+@pytest.mark.parametrize("case", EIGHT_WAVE_RANDOM,
+                         ids=[c[0].name + ("" if c[0].causal else "_noncausal") + ("" if c[1] else "_plain_q")
+                              for c in EIGHT_WAVE_RANDOM])
+def test_eight_wave_random_shapes_sampled_rows(case):
+    w, fold_q, seed = case
+    assert w.S >= 8192 and w.B * w.Hq * -(-w.S // 256) >= 1024
+    _sampled_rows_check(w, seed, fold_q, n_heads=3)
+
+
 # every workload with the pipeline's folded query scale; the FP8 layers also
 # with the plain per-tensor absmax scale of the configs (the kernel's fma form)
 FULL_RUNS = [(n, True) for n in WORKLOADS] + [(n, False) for n in WORKLOADS
