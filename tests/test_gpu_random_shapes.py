@@ -19,6 +19,7 @@ exceed 1e-2 only by as much as that precision allows.
 """
 
 import math
+import os
 
 
 import numpy as np
@@ -63,7 +64,8 @@ def _draw(n: int, seed: int = 2024):
     return cases
 
 
-CASES = _draw(96)
+# (a longer sweep: ATTN_RANDOM_SHAPES=1000 ATTN_RANDOM_SEED=79 python -m pytest -m gpu <this file>)
+CASES = _draw(int(os.environ.get("ATTN_RANDOM_SHAPES", "96")), int(os.environ.get("ATTN_RANDOM_SEED", "2024")))
 
 
 def _id(c):
